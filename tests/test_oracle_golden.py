@@ -1,0 +1,50 @@
+"""The pages' worked arithmetic (tests/golden/pages_arithmetic.json)."""
+import json
+import os
+
+import pytest
+
+G = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_arithmetic.json")))
+
+
+def test_comm_volume_formula(orc):
+    c = G["comm_volume"]
+    b = orc.comm_bytes(c["b_tokens_per_rank"], c["K"], c["H"], c["bytes_per_elem_fp8"])
+    assert b == 7_340_032
+    assert round(b / 1e6, 1) == c["printed_MB"]
+    # the same rows at bf16 double the bytes (combine direction)
+    assert orc.comm_bytes(128, 8, 7168, 2) == 2 * b
+
+
+def test_comm_bandwidth_examples(orc):
+    b = orc.comm_bytes(128, 8, 7168, 1)
+    m = G["ll_measured"]
+    # 7.3 MB in 77 us is the printed ~95 GB/s
+    assert abs(b / (m["latency_us"] * 1e-6) / 1e9 - m["printed_bandwidth_GBps"]) < 1.0
+    # the 80 us budget of the formula section gives 91.8 GB/s; the page rounds
+    # it to "about 95" -- within 4 %, kept as a documented inconsistency
+    c = G["comm_volume"]
+    bw80 = b / (c["printed_budget_us"] * 1e-6) / 1e9
+    assert abs(bw80 - 91.75) < 0.01
+    assert abs(bw80 - c["printed_bandwidth_GBps"]) / c["printed_bandwidth_GBps"] < 0.04
+
+
+def test_eplb_and_rank_shares():
+    e = G["eplb_slots"]
+    assert e["logical"] + e["redundant"] == e["physical"]
+    d = G["ep_degrees"]
+    assert e["physical"] % d["decode_ep"] == 0 and e["physical"] // d["decode_ep"] == 4
+    assert e["physical"] % d["prefill_ep"] == 0 and e["physical"] // d["prefill_ep"] == 9
+    from synth import WORKLOADS
+    assert WORKLOADS["decode_rank_fp8"]["n_ranks"] == d["decode_ep"]
+    assert WORKLOADS["decode_rank_fp8"]["n_local"] == e["physical"] // d["decode_ep"]
+    assert WORKLOADS["prefill_rank_fp8"]["n_ranks"] == d["prefill_ep"]
+    assert WORKLOADS["prefill_rank_fp8"]["n_local"] == e["physical"] // d["prefill_ep"]
+    # the decode rank share's dispatch payload is exactly the pages' 7.3 MB
+    w = WORKLOADS["decode_rank_fp8"]
+    assert w["rows"] * w["H"] * 1 == 7_340_032
+
+
+def test_alignment_example():
+    a = G["dense_ffn_alignment"]
+    assert a["intermediate"] // a["tp"] == a["per_rank"] and a["per_rank"] % a["align"] != 0
