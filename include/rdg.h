@@ -1,0 +1,240 @@
+/*
+ * rdg.h -- C ABI of librdg.so: one GPU's share of a DeepSeek-V3-style
+ * mixture-of-experts layer on AMD MI355X (gfx950).
+ *
+ *   rdg_route        group-limited top-k gating
+ *   rdg_eplb_remap   logical -> physical expert remap (redundant experts)
+ *   rdg_dispatch     token -> expert permutation into a contiguous or masked layout
+ *   rdg_grouped_ffn  grouped gate/up GEMM + SiLU-gated product + down GEMM
+ *   rdg_combine      routing-weighted unpermute-and-sum (optionally polling
+ *                    the down GEMM's per-row-tile completion signals)
+ *
+ * Page names used in the citations below:
+ *   [LEP]  "Large-scale EP: DeepEP, EPLB and two-batch overlap" (SGLang handbook)
+ *   [SBO]  "Single Batch Overlap (SBO): Overlaping of Down GEMM with Combine Send"
+ *          (DeepGEMM pull request)
+ *   [H100] SGLang's DeepSeek-V3/R1 deployment on 96 H100s (Chinese article)
+ *   [DEEP] "DeepEP, fully taken apart" (Chinese deep-dive on DeepEP)
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked "host".  They must be 16-byte
+ *     aligned.  The caller owns (allocates and frees) every buffer, including
+ *     workspaces sized by the *_bytes queries; the library allocates nothing.
+ *   - Every compute call only enqueues work on `stream` (a hipStream_t; NULL is
+ *     the default stream) and returns without waiting.  Argument errors are
+ *     returned synchronously (RDG_EINVAL / RDG_EUNSUPPORTED) and then nothing
+ *     is enqueued.  A failed launch returns RDG_EHIP.
+ *   - Errors found on the device (capacity overflow, signal timeout) are
+ *     written to the layout's status word [code, detail], first error wins;
+ *     rdg_check_status is the one call that waits for the stream.
+ *   - No C++ exception crosses this boundary.
+ */
+#ifndef RDG_H
+#define RDG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* rdg_stream_t; /* the same type as hipStream_t */
+
+enum {
+    RDG_OK = 0,
+    RDG_EINVAL = -1,       /* bad argument: nothing was enqueued */
+    RDG_ECAPACITY = -2,    /* rows did not fit the preallocated layout (device status) */
+    RDG_ETIMEOUT = -3,     /* a polled signal never reached its threshold (device status) */
+    RDG_EHIP = -4,         /* the HIP runtime refused a launch or a query */
+    RDG_EUNSUPPORTED = -5  /* a valid but unimplemented combination of sizes / types */
+};
+
+enum { RDG_F32 = 0, RDG_BF16 = 1, RDG_FP8_E4M3 = 2 };   /* element types */
+enum { RDG_CONTIGUOUS = 0, RDG_MASKED = 1 };            /* layout kinds */
+
+/* A dispatch layout ([LEP] DeepEP modes paragraph: the contiguous layout
+ * orders tokens by expert for dynamic shapes, the masked layout keeps fixed
+ * shapes and marks the valid rows; [H100] "DeepGEMM integration").
+ * Filled by the caller: the scalar fields and the buffer pointers.  Written
+ * by rdg_dispatch / rdg_layout_dense: the buffers' contents.
+ *
+ *   kind      RDG_CONTIGUOUS: expert e's rows are [offsets[e], offsets[e] +
+ *             masked_m[e]), segments padded to block_m rows.
+ *             RDG_MASKED: expert e owns rows [e*m_max, (e+1)*m_max); the first
+ *             masked_m[e] are valid.
+ *   n_local   experts held by this GPU (1..1024)
+ *   block_m   contiguous: padding granularity in rows, a multiple of 16 (128
+ *             lets the GEMMs use their largest row tile)
+ *   m_max     masked: rows per expert
+ *   m_cap     rows of x_perm / y / row_src.  Masked: n_local*m_max.
+ *             Contiguous: at least n_rows + n_local*(block_m-1) never overflows.
+ *   n_rows    the number of (token, slot) entries dispatched, T*K (sizes grids)
+ *   counts    [n_local]   rows routed to each expert
+ *   offsets   [n_local+1] first row of each expert's segment
+ *   masked_m  [n_local]   rows kept for each expert (counts clipped to capacity)
+ *   pos       [T*K]       layout row of entry t*K+k, or -1 (not local / dropped)
+ *   row_src   [m_cap]     entry t*K+k stored in each row, or -1 (padding)
+ *   status    [2]         {code, detail}; cleared by rdg_dispatch
+ *   work      rdg_dispatch_workspace_bytes(T, K, n_local) bytes
+ */
+typedef struct rdg_layout {
+    int32_t kind, n_local, block_m, m_max, m_cap, n_rows;
+    int32_t* counts;
+    int32_t* offsets;
+    int32_t* masked_m;
+    int32_t* pos;
+    int32_t* row_src;
+    int32_t* status;
+    void* work;
+} rdg_layout;
+
+/* Group-limited top-k gating ([DEEP] "group-limited gating": pick the best
+ * groups first, then the top-K experts inside them; [DEEP] "EP": the token's
+ * output is the routing-weighted sum over its K experts).
+ *   logits    [B, N] fp32, row-major
+ *   n_group   groups of N/n_group consecutive experts; topk_group of them kept
+ *   K         experts per token (K <= topk_group*N/n_group, K <= 32)
+ *   scale     the renormalised weights sum to this
+ *   topk_ids  [B, K] int32 out: experts in (score desc, id asc) order
+ *   topk_w    [B, K] fp32 out
+ * Score: sigmoid evaluated in fp64 and rounded once to fp32 (a fixed
+ * evaluation, bit-identical wherever it is implemented); group score: fp32
+ * sum of the group's two largest scores; ties go to the lower index.
+ * Limits: N <= 1024, n_group <= 64.  B = 0 is a no-op. */
+int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
+              int32_t* topk_ids, float* topk_w, rdg_stream_t stream);
+
+/* EPLB logical -> physical remap ([LEP] self-test answer 3 and the EPLB
+ * paragraph: 256 logical experts in 288 physical slots, popular experts
+ * replicated, each copy taking a share; [H100] "EPLB").
+ *   ids        [T, K] logical expert ids (-1: entry not sent to this GPU)
+ *   token_gidx [T] int64 global token index; replica = gidx mod n_replica[e]
+ *   log2phy    [n_logical, r_max] physical id of each replica
+ *   n_replica  [n_logical] replicas per logical expert (1..r_max)
+ *   local_ids  [T, K] out: physical id - phys_begin when it lies in
+ *              [phys_begin, phys_begin + n_local), else -1
+ * May run in place (local_ids == ids). */
+int rdg_eplb_remap(const int32_t* ids, const int64_t* token_gidx, int T, int K, const int32_t* log2phy,
+                   const int32_t* n_replica, int r_max, int n_logical, int phys_begin, int n_local,
+                   int32_t* local_ids, rdg_stream_t stream);
+
+/* Bytes of rdg_layout.work for a dispatch of T tokens x K slots over n_local experts. */
+size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);
+
+/* Dispatch ([LEP] self-test answer 1: the contiguous layout needs a permute
+ * that orders tokens by expert; [H100] "DeepEP-based EP": exceeding a
+ * preallocated fixed buffer is a runtime error; [DEEP] "How large is the
+ * traffic": each token's H-vector goes to each of its K experts).
+ *   x         [T, H] tokens: fp32, bf16 or fp8 e4m3 (dtype)
+ *   x_scales  [T, H/128] fp32 block scales (fp8 only, else NULL)
+ *   ids       [T, K] local expert ids in [0, n_local), -1 = skip
+ *   x_perm    [m_cap, H] out (dtype); x_perm_scales [m_cap, H/128] (fp8)
+ * Rows of one expert keep their (t, k) order (a stable counting sort), so the
+ * layout is deterministic.  Overflow drops the extra rows and sets status
+ * RDG_ECAPACITY (masked: detail = the largest count; contiguous: detail =
+ * the rows needed).  Padding rows of x_perm are left untouched.
+ * H must be a multiple of 16 (fp8: of 128).  T = 0 is allowed. */
+int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
+                 const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream);
+
+/* Describe T rows as one expert's segment (rows [0, T)), for running a dense
+ * FFN -- the shared expert -- through rdg_grouped_ffn with n_local = 1.
+ * Writes counts, offsets, masked_m and the work area; L->kind must be
+ * RDG_CONTIGUOUS, L->n_local 1, L->m_cap >= T, L->n_rows = T. */
+int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
+
+/* Grouped expert FFN over a layout (the expert FFN of [DEEP] "EP"; the
+ * contiguous and masked grouped GEMMs of [H100] "DeepGEMM integration"; the
+ * fp8 "1d2d" block-scaled masked GEMM and the signalled down GEMM of [SBO]
+ * sections 2-3).  For every valid row r of expert e:
+ *   h[r] = silu(x[r] W1_e^T) * (x[r] W3_e^T)      (stored in h_ws)
+ *   y[r] = h[r] W2_e^T                             (stored in y)
+ * Weights are K-major: W1, W3 [n_local, I, H]; W2 [n_local, H, I].
+ * dtype RDG_F32: everything fp32.  RDG_BF16: bf16 operands, fp32
+ * accumulation, h and y bf16.  RDG_FP8_E4M3: e4m3 operands, x_perm_scales
+ * [m_cap, H/128], weight scales W1_s, W3_s [n_local, I/128, H/128] and
+ * W2_s [n_local, H/128, I/128]; every 128-long partial product is scaled by
+ * its activation and weight block scales in fp32; h is re-quantised to e4m3
+ * with 1x128 scales (h_scales_ws [m_cap, I/128]); y is bf16.
+ *   h_ws      [m_cap, I] (dtype's storage: fp32 / bf16 / e4m3)
+ *   y         [m_cap, H] fp32 (RDG_F32) or bf16
+ *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype))] int32, zeroed by the
+ *             caller (rdg_fill_i32) before this call: after the down GEMM
+ *             has stored a row tile's outputs for one column block it adds 1
+ *             to that tile's counter with release ordering at device scope;
+ *             a tile is complete at rdg_signal_threshold(H, dtype).
+ * Rows outside [offsets[e], offsets[e] + masked_m[e]) are neither read nor
+ * written.  H and I must be multiples of 128. */
+int rdg_grouped_ffn(const rdg_layout* L, int dtype, int H, int I, const void* x_perm, const float* x_perm_scales,
+                    const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
+                    const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,
+                    rdg_stream_t stream);
+
+/* The two stages of rdg_grouped_ffn as separate launches (same arguments
+ * and rules): the gate/up GEMM with the SiLU-gated product writing h (and
+ * its fp8 scales), and the down GEMM reading h and writing y (optionally
+ * signalling).  rdg_grouped_ffn = rdg_grouped_gate_up then rdg_grouped_down
+ * on the same stream. */
+int rdg_grouped_gate_up(const rdg_layout* L, int dtype, int H, int I, const void* x_perm, const float* x_perm_scales,
+                        const void* W1, const void* W3, const float* W1_s, const float* W3_s, void* h_ws,
+                        float* h_scales_ws, rdg_stream_t stream);
+int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h_ws, const float* h_scales_ws,
+                     const void* W2, const float* W2_s, void* y, int32_t* signals, rdg_stream_t stream);
+
+/* Rows per signal counter and the counter value that means "row tile done",
+ * for the down GEMM of rdg_grouped_ffn on this layout. */
+int rdg_signal_rows(const rdg_layout* L, int dtype);
+int rdg_signal_threshold(int H, int dtype);
+
+/* Combine ([DEEP] "EP": weighted sum back to the token; [DEEP] "why is
+ * combine slower": transfer plus weighted reduction; [DEEP] "limitations":
+ * bf16 pre-reduction is imprecise and non-deterministic, so the sum here is
+ * fp32, in k order, rounded once; [SBO] section 2: poll each row tile's
+ * counter until it reaches the threshold before using its rows).
+ *   out[t] = shared_out[t] + sum_{k: pos[t,k] >= 0} topk_w[t,k] * y[pos[t,k]]
+ *   y          [m_cap, H] (y_dtype: RDG_F32 or RDG_BF16)
+ *   topk_w     [T, K] fp32
+ *   shared_out [T, H] in out_dtype, or NULL
+ *   out        [T, H] out_dtype (RDG_F32 or RDG_BF16)
+ *   signals    NULL, or the counters given to rdg_grouped_ffn, with
+ *              threshold and a timeout in microseconds (a tile still
+ *              incomplete then is skipped and status = RDG_ETIMEOUT with
+ *              detail = the tile index)
+ *   max_blocks 0 = one wavefront per token; else at most this many 256-thread
+ *              workgroups loop over the tokens (keeps a polling combine from
+ *              occupying the CUs the down GEMM needs).
+ * The polling form may run on another stream concurrently with the down
+ * GEMM, which must have been enqueued first. */
+int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
+                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int threshold,
+                int64_t timeout_us, int max_blocks, rdg_stream_t stream);
+
+/* fp8 e4m3 block quantiser (the "1d2d" scales of [SBO] section 3): blocks of
+ * block_rows x 128 (1 for activations, 128 for weights); scale = amax/448 in
+ * fp32 (1 for an all-zero block), code = round-to-nearest-even of
+ * clamp(v / scale, -448, 448).
+ *   src     [rows, cols] fp32 or bf16 (src_dtype)
+ *   q       [rows, cols] e4m3 codes out
+ *   scales  [ceil(rows/block_rows), cols/128] fp32 out
+ * cols must be a multiple of 128; block_rows is 1 or 128. */
+int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,
+                     float* scales, rdg_stream_t stream);
+
+/* Fill n int32 words with value (a kernel, so it is safe inside captured graphs). */
+int rdg_fill_i32(int32_t* p, int32_t value, int64_t n, rdg_stream_t stream);
+
+/* Wait for the stream, then copy the status word {code, detail} to the host
+ * array host_status[2].  Returns the code (RDG_OK when no error was found). */
+int rdg_check_status(const int32_t* status, int32_t* host_status, rdg_stream_t stream);
+
+/* A static string for a return or status code. */
+const char* rdg_strerror(int code);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int rdg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RDG_H */

@@ -98,21 +98,29 @@ double orc_fp8_decode(uint8_t c) {
     return s ? -v : v;
 }
 
-/* value -> e4m3fn: the nearest of the 127 non-negative finite codes to |v|,
- * ties to the code with an even mantissa, then the sign bit.  The caller
- * clamps to [-448, 448] first (the scale rule below guarantees it). */
+/* value -> e4m3fn, round to nearest, ties to even, from the definition:
+ * the format keeps 4 significant bits; for |v| in [2^e, 2^(e+1)), e >= -6,
+ * the quantum is 2^(e-3), and below 2^-6 it is fixed at 2^-9 (subnormals).
+ * The rounded magnitude is then written as sign, biased exponent, mantissa.
+ * The caller clamps to [-448, 448] first (the scale rule guarantees it). */
 uint8_t orc_fp8_encode(double v) {
-    double a = fabs(v), best_d = INFINITY;
-    int best = 0, c;
-    for (c = 0; c < 127; ++c) {
-        double d = fabs(orc_fp8_decode((uint8_t)c) - a);
-        if (d < best_d || (d == best_d && (c & 1) == 0 && (best & 1) == 1)) {
-            best_d = d;
-            best = c;
-        }
+    double a = fabs(v), q, r;
+    int e, code;
+    if (a < ldexp(1.0, -6)) {
+        q = ldexp(1.0, -9);
+    } else {
+        frexp(a, &e);           /* a = m * 2^e, m in [0.5, 1): |v| in [2^(e-1), 2^e) */
+        q = ldexp(1.0, e - 4);  /* 4 significant bits */
     }
-    if (v < 0 || (v == 0 && signbit(v))) best |= 0x80;
-    return (uint8_t)best;
+    r = nearbyint(a / q) * q;   /* exact scaling by a power of two; half to even */
+    if (r < ldexp(1.0, -6)) {
+        code = (int)(r / ldexp(1.0, -9));          /* subnormal: m * 2^-9, m = 0..7 */
+    } else {
+        frexp(r, &e);                              /* r in [2^(e-1), 2^e) */
+        code = ((e - 1 + 7) << 3) | (int)(ldexp(r, -(e - 1)) * 8.0 - 8.0);
+    }
+    if (v < 0 || (v == 0 && signbit(v))) code |= 0x80;
+    return (uint8_t)code;
 }
 
 /* Block quantiser (the "1d2d" format of the masked fp8 grouped GEMM,

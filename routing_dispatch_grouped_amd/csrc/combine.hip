@@ -1,0 +1,138 @@
+// Combine: routing-weighted unpermute-and-sum.
+//
+// What it computes (DeepEP deep-dive, EP section: expert outputs are
+// summed back to their token weighted by the routing weights; section "why
+// is combine slower than dispatch": combine is transfer plus a weighted
+// reduction; section "limitations": bf16 pre-reduction loses precision and
+// is non-deterministic -- so here the sum is fp32, in slot order, rounded
+// once; DeepGEMM single-batch-overlap pull request, section 2: the consumer
+// polls a per-row-block counter until it reaches its threshold).
+//
+//   out[t] = shared_out[t] + sum_{k: pos[t,k] >= 0} w[t,k] * y[pos[t,k]]
+//
+// Design for CDNA4: one wave per token; each lane owns 8 consecutive
+// features per step (a 16-byte bf16 vector), gathers the K expert rows for
+// them, accumulates in fp32 and writes once.  In the polling form, lane 0
+// waits (acquire, device scope) on the counter of each row tile the token
+// reads; a bounded wait turns a tile that never completes into a status
+// code instead of a hang.
+#include "rdg_internal.h"
+
+namespace rdg {
+namespace {
+
+template <int YDT>
+__device__ __forceinline__ void load8(const void* y, size_t row, int H, int v, float* out) {
+    if (YDT == RDG_BF16) {
+        const uint4 q = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H)[v];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+            out[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    } else {
+        const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(y) + row * H) + 2 * v;
+        const float4 a = p[0], b = p[1];
+        out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+        out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+    }
+}
+
+template <int ODT>
+__device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const float* acc) {
+    if (ODT == RDG_BF16) {
+        uint4 q;
+        q.x = f32_to_bf16(acc[0]) | (f32_to_bf16(acc[1]) << 16);
+        q.y = f32_to_bf16(acc[2]) | (f32_to_bf16(acc[3]) << 16);
+        q.z = f32_to_bf16(acc[4]) | (f32_to_bf16(acc[5]) << 16);
+        q.w = f32_to_bf16(acc[6]) | (f32_to_bf16(acc[7]) << 16);
+        reinterpret_cast<uint4*>(static_cast<uint16_t*>(o) + row * H)[v] = q;
+    } else {
+        float4* p = reinterpret_cast<float4*>(static_cast<float*>(o) + row * H) + 2 * v;
+        p[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        p[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    }
+}
+
+// Lane 0 waits for a counter; returns false on timeout.
+__device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_ticks) {
+    const uint64_t t0 = wall_clock64();
+    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < threshold) {
+        if (wall_clock64() - t0 > timeout_ticks) return false;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return true;
+}
+
+template <int YDT, int ODT>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ w, int T, int K, int H,
+                                                 const void* __restrict__ shared_out, void* __restrict__ out,
+                                                 const int32_t* signals, int rows_per_sig, int threshold,
+                                                 uint64_t timeout_ticks, int32_t* status) {
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int nvec = H / 8;
+    for (int t = blockIdx.x * 4 + wv; t < T; t += gridDim.x * 4) {
+        int p = -1;
+        float wt = 0.0f;
+        if (lane < K) {
+            p = pos[(size_t)t * K + lane];
+            wt = w[(size_t)t * K + lane];
+        }
+        if (signals != nullptr) {
+            for (int k = 0; k < K; ++k) {
+                const int pk = __shfl(p, k);
+                if (pk < 0) continue;
+                int ok = 1;
+                if (lane == 0) {
+                    ok = wait_counter(signals + pk / rows_per_sig, threshold, timeout_ticks) ? 1 : 0;
+                    if (!ok) set_status(status, RDG_ETIMEOUT, pk / rows_per_sig);
+                }
+                ok = __shfl(ok, 0);
+                if (!ok && lane == k) p = -1;  // skip the incomplete row
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        }
+        for (int v = lane; v < nvec; v += kWave) {
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            for (int k = 0; k < K; ++k) {
+                const int pk = __shfl(p, k);
+                const float wk = __shfl(wt, k);
+                if (pk < 0) continue;
+                float yv[8];
+                load8<YDT>(y, (size_t)pk, H, v, yv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += wk * yv[i];
+            }
+            if (shared_out != nullptr) {
+                float sv[8];
+                load8<ODT>(shared_out, (size_t)t, H, v, sv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += sv[i];
+            }
+            store8<ODT>(out, (size_t)t, H, v, acc);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
+                          const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
+                          int threshold, uint64_t timeout_ticks, int max_blocks, int32_t* status, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    int blocks = (T + 3) / 4;
+    if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+#define RDG_COMBINE(YD, OD)                                                                                     \
+    k_combine<YD, OD><<<blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, signals, rows_per_sig,        \
+                                              threshold, timeout_ticks, status)
+    if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_COMBINE(RDG_BF16, RDG_BF16);
+    else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_COMBINE(RDG_BF16, RDG_F32);
+    else if (y_dt == RDG_F32 && out_dt == RDG_F32) RDG_COMBINE(RDG_F32, RDG_F32);
+    else return hipErrorInvalidValue;
+#undef RDG_COMBINE
+    return hipGetLastError();
+}
+
+}  // namespace rdg

@@ -1,0 +1,311 @@
+// Dispatch: EPLB remap, the layout builder (a stable counting sort by
+// expert) and the payload permutation.
+//
+// What it computes (SGLang large-scale EP chapter, self-test answer 1 and
+// the DeepEP-modes paragraph: the contiguous layout orders tokens by expert
+// for the dynamic shapes of prefill, the masked layout keeps fixed shapes
+// with a mask of valid rows for decode; H100 deployment article, "DeepEP-
+// based EP": overflowing a preallocated fixed buffer is an error; DeepEP
+// deep-dive, "normal kernels": a counting pass precedes the transfer, which
+// there costs a device-to-host wait -- here the counts stay on the device).
+//
+// Design for CDNA4, three launches, no host round trip:
+//   1. rank:    one wave per chunk of entries; within each 64-entry piece the
+//               lanes holding the same expert find each other with one ballot
+//               per bit of the expert id, which gives each entry its rank
+//               among equal experts in flat order; a per-wave LDS counter
+//               carries ranks across pieces.  Writes the chunk histograms.
+//   2. scan:    one workgroup turns the chunk histograms into per-chunk bases,
+//               counts, padded offsets, masked_m, capacity status and the row
+//               tile tables used by the grouped GEMM.
+//   3. scatter: one wave per token computes its K destinations and copies the
+//               token's row once from HBM into each of them (16-byte vectors).
+#include "rdg_internal.h"
+
+namespace rdg {
+namespace {
+
+__global__ __launch_bounds__(256) void k_remap(const int32_t* __restrict__ ids, const int64_t* __restrict__ gidx,
+                                               int T, int K, const int32_t* __restrict__ log2phy,
+                                               const int32_t* __restrict__ n_rep, int r_max, int n_logical,
+                                               int phys_begin, int n_local, int32_t* out) {
+    int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= (int64_t)T * K) return;
+    int32_t e = ids[i], r = -1;
+    if (e >= 0 && e < n_logical) {
+        const int32_t nr = n_rep[e];
+        if (nr >= 1 && nr <= r_max) {  // a malformed replica count maps the row nowhere
+            int64_t g = gidx[i / K] % nr;
+            if (g < 0) g += nr;
+            const int32_t p = log2phy[(int64_t)e * r_max + g];
+            if (p >= phys_begin && p < phys_begin + n_local) r = p - phys_begin;
+        }
+    }
+    out[i] = r;
+}
+
+__global__ __launch_bounds__(256) void k_fill_i32(int32_t* p, int32_t v, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = v;
+}
+
+// Pass 1.  grid: ceil(n_chunks / 4) workgroups of 4 waves; dynamic LDS: 4 * n_local int32.
+__global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ ids, int64_t n, int n_local, int chunk,
+                                              int n_chunks, int nbits, int32_t* __restrict__ tmp_rank,
+                                              int32_t* __restrict__ chunk_counts, int32_t* __restrict__ row_src,
+                                              int m_cap, int32_t* __restrict__ status) {
+    extern __shared__ int32_t cnt_all[];
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    int32_t* cnt = cnt_all + wv * n_local;
+    const int c = blockIdx.x * 4 + wv;
+
+    // housekeeping spread over the grid: clear the status word, mark all rows as padding
+    if (blockIdx.x == 0 && threadIdx.x == 0 && status) {
+        status[0] = 0;
+        status[1] = 0;
+    }
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < m_cap; i += (int64_t)gridDim.x * blockDim.x)
+        row_src[i] = -1;
+
+    if (c >= n_chunks) return;  // per-wave exit; no workgroup barrier follows
+    for (int e = lane; e < n_local; e += kWave) cnt[e] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    for (int p = 0; p < chunk; p += kWave) {
+        int64_t i = (int64_t)c * chunk + p + lane;
+        int e = -1;
+        if (i < n) {
+            e = ids[i];
+            if (e < 0 || e >= n_local) e = -1;
+        }
+        const uint32_t key = (uint32_t)(e + 1);
+        uint64_t same = ~0ull;
+        for (int b = 0; b < nbits; ++b) {
+            const uint32_t bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        if (e >= 0) {
+            const int base = cnt[e];
+            tmp_rank[i] = base + __popcll(same & lt_mask);
+            if (lane == 63 - __clzll(same)) cnt[e] = base + __popcll(same);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    for (int e = lane; e < n_local; e += kWave) chunk_counts[(size_t)c * n_local + e] = cnt[e];
+}
+
+// Exclusive scan over a 1024-thread workgroup (16 waves).
+__device__ int block_exclusive_scan(int v, int* lds16, int* total) {
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) lds16[wv] = x;
+    __syncthreads();
+    if (wv == 0) {
+        int w = lane < 16 ? lds16[lane] : 0;
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            int y = __shfl_up(w, off);
+            if (lane >= off) w += y;
+        }
+        if (lane < 16) lds16[16 + lane] = w;  // inclusive wave totals
+    }
+    __syncthreads();
+    int before = wv > 0 ? lds16[16 + wv - 1] : 0;
+    int tot = lds16[16 + 15];
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
+__device__ int block_max(int v, int* lds16) {
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
+    if (lane == 0) lds16[wv] = v;
+    __syncthreads();
+    int m = lds16[0];
+    for (int i = 1; i < 16; ++i) m = max(m, lds16[i]);
+    __syncthreads();
+    return m;
+}
+
+// Pass 2.  One workgroup of 1024 threads; thread e owns expert e (n_local <= 1024).
+__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_counts, int n_chunks, int n_local,
+                                               int kind, int block_m, int m_max, int m_cap,
+                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ masked_m, int32_t* __restrict__ tile_off,
+                                               int32_t* __restrict__ status) {
+    __shared__ int lds[32];
+    const int e = threadIdx.x;
+    const bool act = e < n_local;
+    int run = 0;
+    if (act) {
+        for (int c = 0; c < n_chunks; ++c) {
+            int32_t* p = chunk_counts + (size_t)c * n_local + e;
+            int v = *p;
+            *p = run;
+            run += v;
+        }
+        counts[e] = run;
+    }
+    int seg = 0;
+    if (act) seg = kind == RDG_MASKED ? m_max : (run + block_m - 1) / block_m * block_m;
+    int total;
+    int off = block_exclusive_scan(seg, lds, &total);
+    int keep = run;
+    if (kind == RDG_MASKED && keep > m_max) keep = m_max;
+    if (kind == RDG_CONTIGUOUS) {
+        int room = m_cap - off;
+        if (room < 0) room = 0;
+        if (keep > room) keep = room;
+    }
+    if (act) {
+        offsets[e] = off;
+        masked_m[e] = keep;
+    }
+    if (e == 0) offsets[n_local] = total;
+    int worst = block_max(act ? run : 0, lds);
+    if (e == 0) {
+        if (kind == RDG_MASKED && worst > m_max) set_status(status, RDG_ECAPACITY, worst);
+        if (kind == RDG_CONTIGUOUS && total > m_cap) set_status(status, RDG_ECAPACITY, total);
+    }
+    for (int b = 0; b < kNumBT; ++b) {
+        int nt = act ? (keep + kBT[b] - 1) / kBT[b] : 0;
+        int tt;
+        int to = block_exclusive_scan(nt, lds, &tt);
+        if (act) tile_off[b * (n_local + 1) + e] = to;
+        if (e == 0) tile_off[b * (n_local + 1) + n_local] = tt;
+    }
+}
+
+// Pass 3.  One wave per token.  row_bytes: bytes of one x row (a multiple of 16).
+__global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, const float* __restrict__ x_s,
+                                                 int row_bytes, int n_scales, int T, int K,
+                                                 const int32_t* __restrict__ ids, int n_local, int chunk,
+                                                 const int32_t* __restrict__ chunk_base,
+                                                 const int32_t* __restrict__ tmp_rank,
+                                                 const int32_t* __restrict__ offsets,
+                                                 const int32_t* __restrict__ masked_m, int32_t* __restrict__ pos,
+                                                 int32_t* __restrict__ row_src, uint8_t* __restrict__ x_perm,
+                                                 float* __restrict__ x_perm_s) {
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    int p = -1;
+    if (lane < K) {
+        const int64_t i = (int64_t)t * K + lane;
+        const int e = ids[i];
+        if (e >= 0 && e < n_local) {
+            const int r = chunk_base[(size_t)(i / chunk) * n_local + e] + tmp_rank[i];
+            if (r < masked_m[e]) p = offsets[e] + r;
+        }
+        pos[i] = p;
+        if (p >= 0) row_src[p] = (int32_t)i;
+    }
+    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * row_bytes);
+    const int nvec = row_bytes / 16;
+    for (int v = lane; v < nvec; v += kWave) {
+        const uint4 val = src[v];
+        for (int k = 0; k < K; ++k) {
+            const int pk = __shfl(p, k);
+            if (pk >= 0) reinterpret_cast<uint4*>(x_perm + (size_t)pk * row_bytes)[v] = val;
+        }
+    }
+    if (x_s != nullptr) {
+        for (int j = lane; j < n_scales; j += kWave) {
+            const float sv = x_s[(size_t)t * n_scales + j];
+            for (int k = 0; k < K; ++k) {
+                const int pk = __shfl(p, k);
+                if (pk >= 0) x_perm_s[(size_t)pk * n_scales + j] = sv;
+            }
+        }
+    }
+}
+
+__global__ void k_layout_dense(int T, int32_t* counts, int32_t* offsets, int32_t* masked_m, int32_t* tile_off,
+                               int32_t* status) {
+    if (threadIdx.x != 0) return;
+    counts[0] = T;
+    masked_m[0] = T;
+    offsets[0] = 0;
+    offsets[1] = T;
+    for (int b = 0; b < kNumBT; ++b) {
+        tile_off[b * 2 + 0] = 0;
+        tile_off[b * 2 + 1] = (T + kBT[b] - 1) / kBT[b];
+    }
+    if (status) {
+        status[0] = 0;
+        status[1] = 0;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_remap(const int32_t* ids, const int64_t* gidx, int T, int K, const int32_t* log2phy,
+                        const int32_t* n_rep, int r_max, int n_logical, int phys_begin, int n_local,
+                        int32_t* out, hipStream_t s) {
+    int64_t n = (int64_t)T * K;
+    if (n == 0) return hipSuccess;
+    k_remap<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(ids, gidx, T, K, log2phy, n_rep, r_max, n_logical,
+                                                        phys_begin, n_local, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    k_fill_i32<<<(unsigned)blocks, 256, 0, s>>>(p, v, n);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, int T, int H, const int32_t* ids,
+                           int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s) {
+    const int64_t n = (int64_t)T * K;
+    const int chunk = chunk_size_for(n);
+    const int n_chunks = n > 0 ? (int)((n + chunk - 1) / chunk) : 0;
+    uint8_t* ws = static_cast<uint8_t*>(L.work);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(ws);
+    int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local));
+    int32_t* tmp_rank = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local) + ws_chunk_bytes(L.n_local));
+    int nbits = 1;
+    while ((1 << nbits) < L.n_local + 1) ++nbits;
+
+    // pass 1 (also clears status and marks rows as padding)
+    int blocks1 = (n_chunks + 3) / 4;
+    int fill_blocks = (int)((L.m_cap + 255) / 256);
+    if (blocks1 < fill_blocks) blocks1 = fill_blocks < 1024 ? fill_blocks : 1024;
+    if (blocks1 < 1) blocks1 = 1;
+    k_rank<<<blocks1, 256, 4 * L.n_local * sizeof(int32_t), s>>>(ids, n, L.n_local, chunk, n_chunks, nbits,
+                                                                   tmp_rank, chunk_counts, L.row_src, L.m_cap,
+                                                                   L.status);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    k_scan<<<1, 1024, 0, s>>>(chunk_counts, n_chunks, L.n_local, L.kind, L.block_m, L.m_max, L.m_cap, L.counts,
+                              L.offsets, L.masked_m, tile_off, L.status);
+    err = hipGetLastError();
+    if (err != hipSuccess || T == 0) return err;
+    const int n_scales = x_scales ? H / 128 : 0;
+    k_scatter<<<(T + 3) / 4, 256, 0, s>>>(static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales, T, K, ids,
+                                          L.n_local, chunk, chunk_counts, tmp_rank, L.offsets, L.masked_m, L.pos,
+                                          L.row_src, static_cast<uint8_t*>(x_perm), x_perm_scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s) {
+    k_layout_dense<<<1, 64, 0, s>>>(T, L.counts, L.offsets, L.masked_m, static_cast<int32_t*>(L.work), L.status);
+    return hipGetLastError();
+}
+
+}  // namespace rdg

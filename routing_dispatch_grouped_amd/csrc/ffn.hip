@@ -1,0 +1,365 @@
+// Grouped expert FFN: gate/up GEMM with the SiLU-gated product fused into
+// its epilogue, then the down GEMM (optionally signalling each finished row
+// tile).
+//
+// What it computes (DeepEP deep-dive, EP section: each selected expert runs
+// its FFN on the token; H100 deployment article, "DeepGEMM integration": a
+// grouped GEMM over a contiguous layout for prefill and over a masked
+// fixed-shape layout for decode; DeepGEMM single-batch-overlap pull request,
+// section 3: the fp8 masked grouped GEMM with 1-D activation and 2-D weight
+// block scales, and a release-ordered counter per block of rows written once
+// the rows are stored; section 2: the counter is polled by the combine).
+//
+// Design for CDNA4.  A workgroup is four 64-wide waves and owns one row tile
+// (BT rows of one expert) times 128 output columns; wave w owns columns
+// [32w, 32w + 32) as two 16-row MFMA tiles, so the weight rows it streams
+// are read exactly once per row tile, straight from HBM into registers (no
+// LDS: nothing else in the workgroup reuses them).  The token rows are the
+// MFMA's second operand, BT/16 column tiles, shared by the four waves
+// through L2.  Both operands are K-major, so each lane's MFMA operand is one
+// contiguous 16- or 32-byte load.  MFMA: 16x16x4 f32, 16x16x32 bf16, and
+// 16x16x128 fp8 e4m3 (one instruction per 128-long scale block, then the
+// partial sum is promoted into the fp32 accumulator with its activation and
+// weight block scales).  The row-tile -> expert mapping comes from the prefix
+// table the dispatch built, so no host sync is needed for dynamic shapes.
+#include "rdg_internal.h"
+
+namespace rdg {
+namespace {
+
+template <int DT>
+struct Mma;
+
+template <>
+struct Mma<RDG_F32> {
+    using op_t = float;
+    static constexpr int KS = 4, ESZ = 4, U = 8;
+    __device__ static op_t load(const uint8_t* row, int k0, int lane) {
+        return reinterpret_cast<const float*>(row)[k0 + (lane >> 4)];
+    }
+    __device__ static op_t zero() { return 0.0f; }
+    __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<RDG_BF16> {
+    using op_t = bf16x8_t;
+    static constexpr int KS = 32, ESZ = 2, U = 4;
+    __device__ static op_t load(const uint8_t* row, int k0, int lane) {
+        return *reinterpret_cast<const bf16x8_t*>(row + (size_t)(k0 + (lane >> 4) * 8) * 2);
+    }
+    __device__ static op_t zero() { return op_t{}; }
+    __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <>
+struct Mma<RDG_FP8_E4M3> {
+    using op_t = i32x8_t;
+    static constexpr int KS = 128, ESZ = 1, U = 1;
+    __device__ static op_t load(const uint8_t* row, int k0, int lane) {
+        const uint4* p = reinterpret_cast<const uint4*>(row + k0 + (lane >> 4) * 32);
+        uint4 a = p[0], b = p[1];
+        op_t r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        return r;
+    }
+    __device__ static op_t zero() { return op_t{}; }
+    // e4m3 x e4m3 (format code 0 for both), unit block exponents (127 = 2^0)
+    __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+    }
+};
+
+struct KArgs {
+    const int32_t* offsets;
+    const int32_t* masked_m;
+    const int32_t* tile_off;
+    int n_local, Kdim, Nout;
+    const uint8_t* X;     // [rows, Kdim] layout rows
+    const float* Xs;      // fp8: [rows, Kdim/128]
+    const uint8_t* Wa;    // [n_local, Nout, Kdim]  (W1, or W2)
+    const uint8_t* Wb;    // [n_local, Nout, Kdim]  (W3 when gated)
+    const float* Was;     // fp8: [n_local, Nout/128, Kdim/128]
+    const float* Wbs;
+    uint8_t* O;           // [rows, Nout]  (h, or y)
+    float* Os;            // fp8 h scales [rows, Nout/128]
+    int32_t* signals;     // [rows / BT]
+};
+
+template <int DT, int BT, bool GATED, bool SIGNAL>
+__global__ __launch_bounds__(256) void k_ffn(KArgs a) {
+    using M = Mma<DT>;
+    using op_t = typename M::op_t;
+    constexpr int NCT = BT / 16;
+    constexpr int KS = M::KS, U = M::U, ESZ = M::ESZ;
+    // output storage: fp32 layer -> fp32; bf16 -> bf16; fp8: h in e4m3, y in bf16
+    constexpr int OUT_KIND = DT == RDG_F32 ? 0 : (DT == RDG_FP8_E4M3 && GATED) ? 2 : 1;
+
+    const int tile = blockIdx.x;
+    const int n_tiles = a.tile_off[a.n_local];
+    if (tile >= n_tiles) return;  // workgroup-uniform
+    int lo = 0, hi = a.n_local;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_off[mid] <= tile) lo = mid;
+        else hi = mid;
+    }
+    const int e = lo;
+    const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
+    const int row_end = a.offsets[e] + a.masked_m[e];
+    const int f0 = blockIdx.y * 128;
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const int fw = f0 + wv * 32;
+    const size_t wstride = (size_t)a.Kdim * ESZ;
+
+    const uint8_t* arow[2];
+    const uint8_t* brow[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const size_t r = (size_t)e * a.Nout + fw + rt * 16 + (lane & 15);
+        arow[rt] = a.Wa + r * wstride;
+        brow[rt] = GATED ? a.Wb + r * wstride : nullptr;
+    }
+    const uint8_t* xrow[NCT];
+    bool xv[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+        const int r = row0 + ct * 16 + (lane & 15);
+        xv[ct] = r < row_end;
+        xrow[ct] = a.X + (size_t)(xv[ct] ? r : row0) * wstride;
+    }
+
+    f32x4_t accA[2][NCT], accB[2][NCT];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            accA[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accB[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
+
+    const int nkb = a.Kdim / 128;
+    const float* was = nullptr;
+    const float* wbs = nullptr;
+    if (DT == RDG_FP8_E4M3) {
+        was = a.Was + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
+        if (GATED) wbs = a.Wbs + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
+    }
+
+    for (int k0 = 0; k0 < a.Kdim; k0 += KS * U) {
+        op_t ra[U][2], rb[U][2], rx[U][NCT];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                ra[u][rt] = M::load(arow[rt], k0 + u * KS, lane);
+                if (GATED) rb[u][rt] = M::load(brow[rt], k0 + u * KS, lane);
+            }
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) rx[u][ct] = xv[ct] ? M::load(xrow[ct], k0 + u * KS, lane) : M::zero();
+        }
+        if (DT != RDG_FP8_E4M3) {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < NCT; ++ct) {
+                        accA[rt][ct] = M::mma(accA[rt][ct], ra[u][rt], rx[u][ct]);
+                        if (GATED) accB[rt][ct] = M::mma(accB[rt][ct], rb[u][rt], rx[u][ct]);
+                    }
+        } else {
+            const int kb = k0 / 128;
+            const float sa_w = was[kb];
+            const float sb_w = GATED ? wbs[kb] : 0.0f;
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+                const float sx = xv[ct] ? a.Xs[(size_t)(row0 + ct * 16 + (lane & 15)) * nkb + kb] : 0.0f;
+                const float fa = sx * sa_w, fb = sx * sb_w;
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
+                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                    const f32x4_t pa = M::mma(z, ra[0][rt], rx[0][ct]);
+                    accA[rt][ct] += pa * fa;
+                    if (GATED) {
+                        const f32x4_t pb = M::mma(z, rb[0][rt], rx[0][ct]);
+                        accB[rt][ct] += pb * fb;
+                    }
+                }
+            }
+        }
+    }
+
+    // ---------------------------------------------------------------- epilogue
+    // accumulator layout of a 16x16 MFMA tile: lane l holds column (token)
+    // l % 16 and rows (features) 4*(l/16) .. 4*(l/16)+3
+    const int fl = fw + (lane >> 4) * 4;  // + rt*16 + r
+    float val[2][NCT][4];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float g = accA[rt][ct][r];
+                if (GATED) {
+                    const float u = accB[rt][ct][r];
+                    val[rt][ct][r] = g / (1.0f + __expf(-g)) * u;
+                } else {
+                    val[rt][ct][r] = g;
+                }
+            }
+
+    if (OUT_KIND == 2) {
+        __shared__ float red[4][BT];
+        float amax[NCT];
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            float m = 0.0f;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(val[rt][ct][r]));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            if (lane < 16) red[wv][ct * 16 + lane] = m;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = ct * 16 + (lane & 15);
+            amax[ct] = fmaxf(fmaxf(red[0][c], red[1][c]), fmaxf(red[2][c], red[3][c]));
+        }
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = row0 + ct * 16 + (lane & 15);
+            if (row >= row_end) continue;
+            const float s = amax[ct] > 0.0f ? amax[ct] / 448.0f : 1.0f;
+            const float inv = 1.0f / s;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                uint32_t q = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float t = fminf(fmaxf(val[rt][ct][r] * inv, -448.0f), 448.0f);
+                    q |= f32_to_e4m3(t) << (8 * r);
+                }
+                *reinterpret_cast<uint32_t*>(a.O + (size_t)row * a.Nout + fl + rt * 16) = q;
+            }
+            if (wv == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = s;
+        }
+    } else {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int row = row0 + ct * 16 + (lane & 15);
+            if (row >= row_end) continue;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                const size_t idx = (size_t)row * a.Nout + fl + rt * 16;
+                if (OUT_KIND == 0) {
+                    float4 o = make_float4(val[rt][ct][0], val[rt][ct][1], val[rt][ct][2], val[rt][ct][3]);
+                    *reinterpret_cast<float4*>(a.O + idx * 4) = o;
+                } else {
+                    uint2 o;
+                    o.x = f32_to_bf16(val[rt][ct][0]) | (f32_to_bf16(val[rt][ct][1]) << 16);
+                    o.y = f32_to_bf16(val[rt][ct][2]) | (f32_to_bf16(val[rt][ct][3]) << 16);
+                    *reinterpret_cast<uint2*>(a.O + idx * 2) = o;
+                }
+            }
+        }
+    }
+
+    if (SIGNAL) {
+        // every thread's stores are complete and visible device-wide before
+        // the workgroup's single release-ordered increment of the tile counter
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(a.signals + row0 / BT, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int DT, int BT>
+hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
+    constexpr int ESZ = Mma<DT>::ESZ;
+    const int hsz = DT == RDG_F32 ? 4 : DT == RDG_BF16 ? 2 : 1;
+    KArgs g{};
+    g.offsets = c.offsets;
+    g.masked_m = c.masked_m;
+    g.tile_off = c.tile_off;
+    g.n_local = c.n_local;
+    // gate/up: Kdim = H, Nout = I
+    g.Kdim = c.H;
+    g.Nout = c.I;
+    g.X = static_cast<const uint8_t*>(c.x);
+    g.Xs = c.x_s;
+    g.Wa = static_cast<const uint8_t*>(c.W1);
+    g.Wb = static_cast<const uint8_t*>(c.W3);
+    g.Was = c.W1_s;
+    g.Wbs = c.W3_s;
+    g.O = static_cast<uint8_t*>(c.h);
+    g.Os = c.h_s;
+    g.signals = nullptr;
+    (void)ESZ;
+    dim3 block(256);
+    if (c.stages & 1) {
+        dim3 grid1(c.n_tiles_max, c.I / 128);
+        k_ffn<DT, BT, true, false><<<grid1, block, 0, s>>>(g);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (!(c.stages & 2)) return hipSuccess;
+    // down: Kdim = I, Nout = H, input h
+    KArgs d{};
+    d.offsets = c.offsets;
+    d.masked_m = c.masked_m;
+    d.tile_off = c.tile_off;
+    d.n_local = c.n_local;
+    d.Kdim = c.I;
+    d.Nout = c.H;
+    d.X = static_cast<const uint8_t*>(c.h);
+    d.Xs = c.h_s;
+    d.Wa = static_cast<const uint8_t*>(c.W2);
+    d.Wb = nullptr;
+    d.Was = c.W2_s;
+    d.Wbs = nullptr;
+    d.O = static_cast<uint8_t*>(c.y);
+    d.Os = nullptr;
+    d.signals = c.signals;
+    (void)hsz;
+    dim3 grid2(c.n_tiles_max, c.H / 128);
+    if (c.signals)
+        k_ffn<DT, BT, false, true><<<grid2, block, 0, s>>>(d);
+    else
+        k_ffn<DT, BT, false, false><<<grid2, block, 0, s>>>(d);
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
+    switch (c.bt) {
+        case 16: return launch_bt<DT, 16>(c, s);
+        case 32: return launch_bt<DT, 32>(c, s);
+        case 64: return launch_bt<DT, 64>(c, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
+    if (c.n_tiles_max <= 0) return hipSuccess;
+    switch (c.dtype) {
+        case RDG_F32: return launch_dt<RDG_F32>(c, s);
+        case RDG_BF16: return launch_dt<RDG_BF16>(c, s);
+        case RDG_FP8_E4M3: return launch_dt<RDG_FP8_E4M3>(c, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rdg

@@ -1,0 +1,139 @@
+// Internal declarations of librdg: device helpers shared by the kernels and
+// the host-side launchers that the C ABI (abi.hip) calls.  gfx950 only.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "rdg.h"
+
+namespace rdg {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------- formats
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN -> canonical NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// OCP e4m3fn code -> fp32 (S.EEEE.MMM, bias 7, E=0 subnormal, no infinity).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+    uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    return (c & 0x80u) ? -v : v;
+}
+
+// fp32 in [-448, 448] -> e4m3fn code, round to nearest even.  Normal range:
+// keep exponent and the top 3 mantissa bits, round on the 20 dropped bits,
+// rebias 127 -> 7 (a carry moves into the exponent).  Below 2^-6 the grid is
+// 2^-9, and a*2^9 is exact, so rint() rounds it directly.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+    uint32_t u = __float_as_uint(v);
+    uint32_t sign = (u >> 24) & 0x80u;
+    uint32_t au = u & 0x7fffffffu;
+    uint32_t code;
+    if (au < 0x3c800000u) {  // |v| < 2^-6
+        code = (uint32_t)__builtin_rintf(__uint_as_float(au) * 512.0f);
+    } else {
+        uint32_t r = au >> 20;
+        uint32_t rem = au & 0xfffffu;
+        r += (rem > 0x80000u) || (rem == 0x80000u && (r & 1u));
+        code = r - (120u << 3);
+    }
+    return sign | code;
+}
+
+// ---------------------------------------------------------------- waves
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        uint32_t lo = __shfl_xor((uint32_t)x, off);
+        uint32_t hi = __shfl_xor((uint32_t)(x >> 32), off);
+        uint64_t o = ((uint64_t)hi << 32) | lo;
+        x = o > x ? o : x;
+    }
+    return x;
+}
+
+__device__ __forceinline__ float wave_max_f32(float x) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
+
+// First error wins: code into st[0] (if still 0), then its detail into st[1].
+__device__ __forceinline__ void set_status(int32_t* st, int code, int detail) {
+    if (st != nullptr && atomicCAS(st, 0, code) == 0) atomicExch(st + 1, detail);
+}
+
+// ---------------------------------------------------------------- workspace
+// The layout's work area: per-row-tile prefix tables for the GEMM row tiles
+// {16, 32, 64, 128} (kNumBT x (n_local+1) int32), the per-chunk counts of the
+// counting sort (kMaxChunks x n_local int32), then one int32 per dispatched
+// entry (its rank inside its chunk).
+constexpr int kNumBT = 4;
+constexpr int kBT[kNumBT] = {16, 32, 64, 128};
+constexpr int kMaxChunks = 64;
+
+__host__ __device__ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+__host__ __device__ inline size_t ws_tile_off_bytes(int n_local) {
+    return align256(sizeof(int32_t) * kNumBT * (size_t)(n_local + 1));
+}
+__host__ __device__ inline size_t ws_chunk_bytes(int n_local) {
+    return align256(sizeof(int32_t) * kMaxChunks * (size_t)n_local);
+}
+__host__ __device__ inline int chunk_size_for(int64_t n_rows) {
+    int64_t pieces = (n_rows + (int64_t)kWave * kMaxChunks - 1) / ((int64_t)kWave * kMaxChunks);
+    if (pieces < 1) pieces = 1;
+    return (int)(pieces * kWave);
+}
+__host__ __device__ inline int bt_index(int bt) { return bt == 16 ? 0 : bt == 32 ? 1 : bt == 64 ? 2 : 3; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns hipSuccess or the launch error.  Arguments are validated by
+// the ABI layer before these are called.
+hipError_t launch_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
+                        int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_remap(const int32_t* ids, const int64_t* gidx, int T, int K, const int32_t* log2phy,
+                        const int32_t* n_rep, int r_max, int n_logical, int phys_begin, int n_local,
+                        int32_t* out, hipStream_t s);
+hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, int T, int H, const int32_t* ids,
+                           int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s);
+hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+hipError_t launch_quantize(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
+                           float* scales, hipStream_t s);
+
+struct FfnCall {
+    const int32_t* offsets;
+    const int32_t* masked_m;
+    const int32_t* tile_off;  // prefix table for row tile bt
+    int n_local, n_tiles_max, bt;
+    int dtype, H, I;
+    const void *x, *W1, *W3, *W2;
+    const float *x_s, *W1_s, *W3_s, *W2_s;
+    void* h;
+    float* h_s;
+    void* y;
+    int32_t* signals;
+    int stages;  // bit 0: gate/up, bit 1: down
+};
+hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+
+hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
+                          const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
+                          int threshold, uint64_t timeout_ticks, int max_blocks, int32_t* status, hipStream_t s);
+
+}  // namespace rdg

@@ -1,0 +1,181 @@
+"""Shared plumbing for the GPU parity tests: run the HIP path through the C
+ABI, gather host copies, and run the oracle on the same seeded inputs.
+Nothing here computes a step of the method."""
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+DEV = "cuda"
+
+
+def rdg():
+    import routing_dispatch_grouped_amd as m
+    return m
+
+
+def dt_code(cfg):
+    m = rdg()
+    return {"f32": m.RDG_F32, "bf16": m.RDG_BF16, "fp8": m.RDG_FP8_E4M3}[cfg["dtype"]]
+
+
+def np_of(t):
+    """Tensor -> numpy in storage form (bf16 -> uint16 bits, fp8 -> uint8 codes)."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return t.view(torch.uint8).numpy()
+    return t.numpy()
+
+
+def out_as_f64(arr):
+    return oracle.bf16_decode(arr) if arr.dtype == np.uint16 else arr.astype(np.float64)
+
+
+def torch_dtype(dt):
+    m = rdg()
+    return {m.RDG_F32: torch.float32, m.RDG_BF16: torch.bfloat16, m.RDG_FP8_E4M3: torch.uint8}[dt]
+
+
+class ExpertSet:
+    """Stacked device weights of n experts ([n, I, H], [n, I, H], [n, H, I]).
+
+    fp32/bf16 workloads store them as generated.  fp8 workloads generate fp32
+    weights, quantise them on the device with rdg_quantize_fp8, and keep the
+    fp32 originals' seeds so the oracle can quantise its own copy."""
+
+    def __init__(self, cfg, expert_ids, device=DEV, shared=False):
+        m = rdg()
+        self.cfg, self.ids, self.shared = cfg, list(expert_ids), shared
+        H = cfg["H"]
+        I = cfg["shared_I"] if shared else cfg["I"]
+        self.H, self.I = H, I
+        n = len(self.ids)
+        self.fp8 = cfg["dtype"] == "fp8"
+        sdt = torch.uint8 if self.fp8 else synth.storage_dtype(cfg)
+        self.W1 = torch.empty((n, I, H), dtype=sdt, device=device)
+        self.W3 = torch.empty((n, I, H), dtype=sdt, device=device)
+        self.W2 = torch.empty((n, H, I), dtype=sdt, device=device)
+        self.s1 = self.s3 = self.s2 = None
+        if self.fp8:
+            f = dict(dtype=torch.float32, device=device)
+            self.s1 = torch.empty((n, I // 128, H // 128), **f)
+            self.s3 = torch.empty((n, I // 128, H // 128), **f)
+            self.s2 = torch.empty((n, H // 128, I // 128), **f)
+        for j, e in enumerate(self.ids):
+            w = synth.expert_weights(cfg, e, device=device, shared=shared)
+            if not self.fp8:
+                self.W1[j].copy_(w["W1"]); self.W3[j].copy_(w["W3"]); self.W2[j].copy_(w["W2"])
+            else:
+                for name, dst, sc in (("W1", self.W1, self.s1), ("W3", self.W3, self.s3), ("W2", self.W2, self.s2)):
+                    m.rdg_quantize_fp8(w[name], m.RDG_F32, 128, dst[j], sc[j])
+            del w
+
+    def oracle_expert(self, j, check_codes=True):
+        """Host copy of expert j in the oracle's storage form (fp8: the
+        oracle's own quantisation of the same fp32 weights; optionally check
+        that the device codes match it bit for bit)."""
+        if not self.fp8:
+            return dict(W1=np_of(self.W1[j]), W3=np_of(self.W3[j]), W2=np_of(self.W2[j]))
+        w = synth.expert_weights(self.cfg, self.ids[j], device=self.W1.device, shared=self.shared)
+        out = {}
+        for name, dev_q, dev_s, key in (("W1", self.W1, self.s1, "1"), ("W3", self.W3, self.s3, "3"),
+                                        ("W2", self.W2, self.s2, "2")):
+            q, s = oracle.quantize_fp8(np_of(w[name]), 128)
+            if check_codes:
+                assert np.array_equal(q, np_of(dev_q[j])), "device weight codes differ from the oracle's"
+                assert np.array_equal(s, np_of(dev_s[j])), "device weight scales differ from the oracle's"
+            out["W" + key], out["s" + key] = q, s
+        return out
+
+
+def quantize_act(x):
+    """Device 1x128 quantisation of activations [T, H]."""
+    m = rdg()
+    T, H = x.shape
+    q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    s = torch.empty((T, H // 128), dtype=torch.float32, device=x.device)
+    src_dt = m.RDG_BF16 if x.dtype == torch.bfloat16 else m.RDG_F32
+    m.rdg_quantize_fp8(x, src_dt, 1, q, s)
+    return q, s
+
+
+def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max=0, shared_out=None,
+               signals=False, max_blocks=0, concurrent=False, timeout_us=2_000_000):
+    """dispatch -> grouped FFN -> combine on the device.  Returns a dict of
+    device tensors (layout, x_perm, h, y, out)."""
+    m = rdg()
+    dt = dt_code(cfg)
+    T, H = x.shape
+    K = local_ids.shape[1]
+    I = cfg["I"]
+    n_local = experts.W1.shape[0]
+    L = m.Layout(kind, n_local, T, K, x.device, block_m=block_m, m_max=m_max)
+    sdt = torch_dtype(dt)
+    x_perm = torch.empty((L.m_cap, H), dtype=sdt, device=x.device)
+    x_perm_s = torch.empty((L.m_cap, H // 128), dtype=torch.float32, device=x.device) if x_s is not None else None
+    m.rdg_dispatch(x, x_s, dt, local_ids, L, x_perm, x_perm_s)
+    h = torch.empty((L.m_cap, I), dtype=sdt, device=x.device)
+    h_s = torch.empty((L.m_cap, I // 128), dtype=torch.float32, device=x.device) if dt == m.RDG_FP8_E4M3 else None
+    ydt = torch.float32 if dt == m.RDG_F32 else torch.bfloat16
+    y = torch.empty((L.m_cap, H), dtype=ydt, device=x.device)
+    sig = None
+    thr = 0
+    if signals:
+        rows = m.rdg_signal_rows(L, dt)
+        sig = torch.empty(((L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=x.device)
+        m.rdg_fill_i32(sig, 0)
+        thr = m.rdg_signal_threshold(H, dt)
+    out_dt = m.RDG_F32 if dt == m.RDG_F32 else m.RDG_BF16
+    out = torch.empty((T, H), dtype=ydt, device=x.device)
+    y_dt = m.RDG_F32 if dt == m.RDG_F32 else m.RDG_BF16
+    if concurrent:
+        s_gemm = torch.cuda.current_stream()
+        s_comb = torch.cuda.Stream()
+        s_comb.wait_stream(s_gemm)  # combine starts after dispatch; it then overlaps the GEMMs
+        m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
+                          experts.s3, experts.s2, h, h_s, y, sig, stream=s_gemm)
+        with torch.cuda.stream(s_comb):
+            m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, thr, timeout_us,
+                          max_blocks, stream=s_comb)
+        s_gemm.wait_stream(s_comb)
+    else:
+        m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
+                          experts.s3, experts.s2, h, h_s, y, sig)
+        m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, thr, timeout_us, max_blocks)
+    return dict(L=L, x_perm=x_perm, x_perm_s=x_perm_s, h=h, h_s=h_s, y=y, out=out, signals=sig, threshold=thr)
+
+
+def run_shared(cfg, x, x_s, shared):
+    """The shared expert as a one-expert dense layout; returns its output [T, H]."""
+    m = rdg()
+    dt = dt_code(cfg)
+    T, H = x.shape
+    I = cfg["shared_I"]
+    L = m.Layout(m.RDG_CONTIGUOUS, 1, T, 1, x.device, block_m=16, m_cap=T)
+    m.rdg_layout_dense(T, L)
+    sdt = torch_dtype(dt)
+    h = torch.empty((T, I), dtype=sdt, device=x.device)
+    h_s = torch.empty((T, I // 128), dtype=torch.float32, device=x.device) if dt == m.RDG_FP8_E4M3 else None
+    ydt = torch.float32 if dt == m.RDG_F32 else torch.bfloat16
+    y = torch.empty((T, H), dtype=ydt, device=x.device)
+    m.rdg_grouped_ffn(L, dt, H, I, x, x_s, shared.W1, shared.W3, shared.W2, shared.s1, shared.s3, shared.s2,
+                      h, h_s, y)
+    return y
+
+
+def check_layout(L, ref, ids_shape):
+    """Bit-exact comparison of a device layout with the oracle's."""
+    assert np.array_equal(np_of(L.counts), ref["counts"]), "counts"
+    assert np.array_equal(np_of(L.offsets), ref["offsets"]), "offsets"
+    assert np.array_equal(np_of(L.masked_m), ref["masked_m"]), "masked_m"
+    n = ids_shape[0] * ids_shape[1]
+    assert np.array_equal(np_of(L.pos)[:n], ref["pos"].ravel()), "pos"
+    assert np.array_equal(np_of(L.row_src)[:L.m_cap], ref["row_src"]), "row_src"
+
+
+def tolerance(cfg):
+    """Max relative error max|out-ref|/max|ref| allowed per tensor."""
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cfg["dtype"]]

@@ -1,0 +1,54 @@
+"""GPU parity of rdg_combine alone on synthetic expert outputs (seeded, not
+produced by the HIP path): fp32 accumulation in slot order vs the oracle's
+fp64 sum, identity-expert and unpermute special cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from harness import DEV, np_of, rdg
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("T,K,E,H,ydt,shared", [(200, 8, 16, 7168, "bf16", True), (33, 4, 8, 256, "f32", False),
+                                                (1, 1, 1, 8, "bf16", False), (1000, 6, 64, 512, "bf16", False)])
+def test_combine_parity(T, K, E, H, ydt, shared):
+    m = rdg()
+    rng = np.random.default_rng([T, K, E, H])
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.1] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    ref_l = oracle.layout(ids, E, oracle.CONTIGUOUS, block_m=16)
+    m_cap = ref_l["m_cap"]
+    if ydt == "bf16":
+        y_h = torch.randn((m_cap, H), dtype=torch.float32).to(torch.bfloat16)
+        sh_h = torch.randn((T, H), dtype=torch.float32).to(torch.bfloat16) if shared else None
+        code = m.RDG_BF16
+    else:
+        y_h = torch.randn((m_cap, H), dtype=torch.float32)
+        sh_h = torch.randn((T, H), dtype=torch.float32) if shared else None
+        code = m.RDG_F32
+    L = m.Layout(m.RDG_CONTIGUOUS, E, T, K, DEV, block_m=16)
+    # the layout comes from the device dispatch (checked bit-exact elsewhere); the
+    # payload rows are the synthetic y below
+    dummy = torch.zeros((T, 16), dtype=torch.float32, device=DEV)
+    xp = torch.zeros((L.m_cap, 16), dtype=torch.float32, device=DEV)
+    m.rdg_dispatch(dummy, None, m.RDG_F32, torch.from_numpy(ids).to(DEV), L, xp)
+    assert np.array_equal(np_of(L.pos), ref_l["pos"].ravel())
+    out = torch.empty((T, H), dtype=y_h.dtype, device=DEV)
+    y_d = y_h.to(DEV)
+    m.rdg_combine(y_d, code, L, torch.from_numpy(w).to(DEV), T, K, H, None if sh_h is None else sh_h.to(DEV),
+                  out, code)
+    ref = oracle.combine(np_of(y_h), ref_l["pos"], w, shared_out=None if sh_h is None else np_of(sh_h),
+                         out_dt=oracle.F32 if ydt == "f32" else oracle.BF16)
+    g = np_of(out)
+    if ydt == "f32":
+        assert oracle.rel_err(g, ref) <= 1e-6
+    else:
+        # fp32 vs fp64 accumulation may move a value across a bf16 rounding
+        # boundary: at most one bf16 step, and rarely
+        gd, rd = oracle.bf16_decode(g), oracle.bf16_decode(ref)
+        step = np.abs(rd) * 2.0 ** -7 + 1e-30
+        assert np.all(np.abs(gd - rd) <= step)
+        assert np.mean(g != ref) < 1e-3

@@ -1,0 +1,246 @@
+"""GPU parity of the whole hot path (route -> [remap] -> dispatch -> grouped
+FFN -> combine, plus the shared expert) against the oracle's definition of
+the layer.  Integers (ids, layouts) bit-exact; outputs within
+max|out-ref|/max|ref| <= 1e-5 (fp32), 2e-2 (bf16), 6e-2 (fp8).
+
+Small workloads are compared on every token; the five full-size workloads
+on every integer output and on a seeded sample of tokens."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import (DEV, ExpertSet, check_layout, dt_code, np_of, out_as_f64, quantize_act, rdg, run_routed,
+                     run_shared, tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+def _route(cfg, logits_np):
+    m = rdg()
+    B = logits_np.shape[0]
+    K = cfg["K"]
+    ids = torch.empty((B, K), dtype=torch.int32, device=DEV)
+    w = torch.empty((B, K), dtype=torch.float32, device=DEV)
+    m.rdg_route(torch.from_numpy(logits_np).to(DEV), cfg["n_group"], cfg["topk_group"], K, cfg["scale"], ids, w)
+    ri, rw = oracle.route(logits_np, cfg["n_group"], cfg["topk_group"], K, cfg["scale"])
+    assert np.array_equal(np_of(ids), ri), "routing ids differ from the oracle"
+    return ids, w, ri, rw
+
+
+def _oracle_experts(es, used):
+    return [es.oracle_expert(j) if j in used else None for j in range(len(es.ids))]
+
+
+def _sample(T, n, seed):
+    if T <= n:
+        return np.arange(T)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(8, T - 8), size=n - 16, replace=False)
+    return np.unique(np.concatenate([np.arange(8), mid, np.arange(T - 8, T)]))
+
+
+def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
+    """Workloads where this GPU holds every expert (the tiny, decode and prefill layers)."""
+    m = rdg()
+    dt = dt_code(cfg)
+    logits = synth.logits(cfg, B)
+    ids, w, ri, rw = _route(cfg, logits)
+    x = synth.x(cfg, B, device=DEV)
+    x_s = None
+    xo = np_of(x)
+    xo_s = None
+    if dt == m.RDG_FP8_E4M3:
+        xq, x_s = quantize_act(x)
+        rq, rs = oracle.quantize_fp8(np_of(x), 1)
+        assert np.array_equal(np_of(xq), rq) and np.array_equal(np_of(x_s), rs)
+        x, xo, xo_s = xq, rq, rs
+    N = cfg["N"]
+    experts = ExpertSet(cfg, range(N))
+    shared = ExpertSet(cfg, [0], shared=True) if cfg["shared_I"] else None
+    sh_out = run_shared(cfg, x, x_s, shared) if shared else None
+    r = run_routed(cfg, x, x_s, ids, w, experts, kind, block_m=block_m, m_max=m_max, shared_out=sh_out)
+    st = m.rdg_check_status(r["L"])
+    ref_l = oracle.layout(ri, N, kind, block_m=block_m, m_max=m_max)
+    assert st == (ref_l["status"], ref_l["detail"])
+    check_layout(r["L"], ref_l, ri.shape)
+    sel = _sample(B, n_sample, seed) if n_sample else np.arange(B)
+    used = set(np.unique(ri[sel]).tolist())
+    ref = oracle.moe_layer(dt, xo, ri, rw, _oracle_experts(experts, used),
+                           shared=shared.oracle_expert(0) if shared else None, x_scales=xo_s, sel=sel)
+    got = np_of(r["out"])[sel]
+    err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
+    print("%s B=%d kind=%d rel_err=%.3e" % (cfg.get("name", cfg["wid"]), B, kind, err), flush=True)
+    assert err <= tolerance(cfg), err
+    return err
+
+
+def _small_cfg(dtype, N=32, n_group=4, topk_group=2, K=4, H=512, I=256, wid=100):
+    return dict(wid=wid, H=H, N=N, n_group=n_group, topk_group=topk_group, K=K, I=I, shared_I=I, dtype=dtype,
+                scale=1.0, logits="normal", name="small_" + dtype)
+
+
+# row tiles 16 / 32 / 64 are picked from the rows per expert (T*K/N): 40*4/32=5,
+# 300*4/32=37.5, 600*4/16=150; the ragged token counts leave partial tiles
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("B,N,kind", [(40, 32, 0), (300, 32, 0), (600, 16, 0), (40, 32, 1), (300, 32, 1),
+                                      (600, 16, 1)])
+def test_small_layers(dtype, B, N, kind):
+    cfg = _small_cfg(dtype, N=N, wid=100 + B + N)
+    m_max = 0
+    if kind == rdg().RDG_MASKED:
+        m_max = ((B + 63) // 64) * 64  # never overflows: a token hits an expert once
+    _full_layer(cfg, B, kind, block_m=128, m_max=m_max)
+
+
+def test_tiny_fp32_workload():
+    cfg = dict(synth.WORKLOADS["tiny_fp32"], name="tiny_fp32")
+    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=16)
+
+
+def test_decode_bf16_workload():
+    cfg = dict(synth.WORKLOADS["decode_bf16"], name="decode_bf16")
+    _full_layer(cfg, cfg["B"], rdg().RDG_MASKED, m_max=cfg["m_max"], n_sample=24, seed=2)
+
+
+def test_prefill_bf16_workload():
+    cfg = dict(synth.WORKLOADS["prefill_bf16"], name="prefill_bf16")
+    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=32, seed=3)
+
+
+# ---------------------------------------------------------------- rank shares
+def rank_share(cfg):
+    """One rank's received tokens under the EPLB placement: route the global
+    batch (checked bit-exact), remap onto the bottleneck rank, and take the
+    tokens that send it rows, in global order, until exactly cfg['rows'] rows
+    (the last token's surplus local rows are marked -1: not sent)."""
+    m = rdg()
+    plan = synth.eplb_plan(cfg)
+    logits = synth.logits(cfg)
+    ids, w, ri, rw = _route(cfg, logits)
+    Tg, K = ri.shape
+    gidx = np.arange(Tg, dtype=np.int64)
+    l2p, nrep = plan["log2phy"], plan["n_replica"]
+    loc = torch.empty((Tg, K), dtype=torch.int32, device=DEV)
+    m.rdg_eplb_remap(ids, torch.from_numpy(gidx).to(DEV), torch.from_numpy(l2p).to(DEV),
+                     torch.from_numpy(nrep).to(DEV), plan["phys_begin"], plan["n_local"], loc)
+    rloc = oracle.eplb_remap(ri, gidx, l2p, nrep, plan["phys_begin"], plan["n_local"])
+    assert np.array_equal(np_of(loc), rloc), "remap differs from the oracle"
+    per_tok = (rloc >= 0).sum(1)
+    toks, taken = [], 0
+    recv_ids = []
+    for t in np.flatnonzero(per_tok > 0):
+        row = ri[t].copy()
+        need = cfg["rows"] - taken
+        if per_tok[t] > need:
+            keep = np.flatnonzero(rloc[t] >= 0)[:need]
+            drop = [k for k in np.flatnonzero(rloc[t] >= 0) if k not in keep]
+            row[drop] = -1
+        toks.append(t)
+        recv_ids.append(row)
+        taken += min(per_tok[t], need)
+        if taken == cfg["rows"]:
+            break
+    toks = np.array(toks)
+    phys2log = np.full(cfg["n_ranks"] * cfg["n_local"], -1)
+    for e in range(cfg["N"]):
+        for r_ in range(nrep[e]):
+            phys2log[l2p[e, r_]] = e
+    local_logical = [int(phys2log[plan["phys_begin"] + s]) for s in range(plan["n_local"])]
+    return dict(plan=plan, tokens=toks, ids=np.stack(recv_ids).astype(np.int32), w=rw[toks], gidx=gidx[toks],
+                rows=taken, local_logical=local_logical, w_dev=w[torch.from_numpy(toks).to(DEV)].contiguous())
+
+
+def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False, n_sample=32, seed=0):
+    m = rdg()
+    share = rank_share(cfg)
+    assert share["rows"] == cfg["rows"]
+    T = len(share["tokens"])
+    plan = share["plan"]
+    x_bf = synth.x(cfg, T, device=DEV)
+    xq, x_s = quantize_act(x_bf)
+    rq, rs = oracle.quantize_fp8(np_of(x_bf), 1)
+    assert np.array_equal(np_of(xq), rq) and np.array_equal(np_of(x_s), rs)
+    ids_d = torch.from_numpy(share["ids"]).to(DEV)
+    loc = torch.empty_like(ids_d)
+    m.rdg_eplb_remap(ids_d, torch.from_numpy(share["gidx"]).to(DEV), torch.from_numpy(plan["log2phy"]).to(DEV),
+                     torch.from_numpy(plan["n_replica"]).to(DEV), plan["phys_begin"], plan["n_local"], loc)
+    rloc = oracle.eplb_remap(share["ids"], share["gidx"], plan["log2phy"], plan["n_replica"], plan["phys_begin"],
+                             plan["n_local"])
+    assert np.array_equal(np_of(loc), rloc)
+    assert int((rloc >= 0).sum()) == cfg["rows"]
+    experts = ExpertSet(cfg, share["local_logical"])
+    r = run_routed(cfg, xq, x_s, loc, share["w_dev"], experts, kind, block_m=block_m, m_max=m_max,
+                   signals=signals, concurrent=concurrent, max_blocks=64 if concurrent else 0)
+    st = m.rdg_check_status(r["L"])
+    ref_l = oracle.layout(rloc, plan["n_local"], kind, block_m=block_m, m_max=m_max)
+    assert st == (ref_l["status"], ref_l["detail"])
+    check_layout(r["L"], ref_l, rloc.shape)
+    sel = _sample(T, n_sample, seed)
+    oe = [experts.oracle_expert(j) for j in range(plan["n_local"])]
+    ref = oracle.moe_layer(oracle.FP8, rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
+    err = oracle.rel_err(out_as_f64(np_of(r["out"])[sel]), out_as_f64(ref))
+    print("%s rows=%d tokens=%d rel_err=%.3e" % (cfg["name"], cfg["rows"], T, err), flush=True)
+    assert err <= tolerance(cfg), err
+    return r, share, experts, (xq, x_s, loc)
+
+
+def test_decode_rank_fp8_workload():
+    cfg = dict(synth.WORKLOADS["decode_rank_fp8"], name="decode_rank_fp8")
+    _rank_layer(cfg, rdg().RDG_MASKED, m_max=cfg["m_max"])
+
+
+def test_prefill_rank_fp8_workload_sbo():
+    m = rdg()
+    cfg = dict(synth.WORKLOADS["prefill_rank_fp8"], name="prefill_rank_fp8")
+    r, share, experts, (xq, x_s, loc) = _rank_layer(cfg, m.RDG_CONTIGUOUS, block_m=128, signals=True,
+                                                    concurrent=True)
+    # every row tile's counter reached the threshold exactly; unused counters stayed 0
+    L = r["L"]
+    rows = m.rdg_signal_rows(L, m.RDG_FP8_E4M3)
+    sig = np_of(r["signals"])
+    off = np_of(L.offsets)
+    mm = np_of(L.masked_m)
+    want = np.zeros_like(sig)
+    for e in range(len(mm)):
+        for j in range((mm[e] + rows - 1) // rows):
+            want[(off[e] + j * rows) // rows] = r["threshold"]
+    assert np.array_equal(sig, want)
+    # the signalled, concurrent run equals the plain sequential run bit for bit
+    r2 = run_routed(cfg, xq, x_s, loc, share["w_dev"], experts, m.RDG_CONTIGUOUS, block_m=128)
+    assert torch.equal(r["out"], r2["out"])
+    assert torch.equal(r["y"], r2["y"])
+    # shared expert on the rank's own tokens
+    x_own = synth.x(cfg, cfg["own_tokens"], device=DEV, tensor=10)
+    oq, os_ = quantize_act(x_own)
+    shared = ExpertSet(cfg, [0], shared=True)
+    ys = run_shared(cfg, oq, os_, shared)
+    sel = _sample(cfg["own_tokens"], 16, 5)
+    rq, rs = oracle.quantize_fp8(np_of(x_own), 1)
+    ref = oracle.moe_layer(oracle.FP8, rq, np.full((cfg["own_tokens"], 1), -1, np.int32),
+                           np.zeros((cfg["own_tokens"], 1), np.float32), [None], shared=shared.oracle_expert(0),
+                           x_scales=rs, sel=sel)
+    err = oracle.rel_err(out_as_f64(np_of(ys)[sel]), out_as_f64(ref))
+    print("prefill_rank_fp8 shared expert rel_err=%.3e" % err, flush=True)
+    assert err <= tolerance(cfg)
+
+
+def test_sbo_timeout_is_reported_not_hung():
+    """A threshold the producer can never reach: the combine gives up after
+    its timeout, flags RDG_ETIMEOUT, and every kernel still exits."""
+    m = rdg()
+    cfg = _small_cfg("bf16", N=8, wid=77)
+    B = 64
+    logits = synth.logits(cfg, B)
+    ids, w, ri, _ = _route(cfg, logits)
+    x = synth.x(cfg, B, device=DEV)
+    experts = ExpertSet(cfg, range(8))
+    r = run_routed(cfg, x, None, ids, w, experts, m.RDG_CONTIGUOUS, block_m=128, signals=True)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    out = torch.empty_like(r["out"])
+    m.rdg_combine(r["y"], m.RDG_BF16, r["L"], w, B, cfg["K"], cfg["H"], None, out, m.RDG_BF16, r["signals"],
+                  r["threshold"] + 1, 2000, 4)
+    code, detail = m.rdg_check_status(r["L"])
+    assert code == m.RDG_ETIMEOUT
+    assert 0 <= detail < len(r["signals"])
