@@ -101,7 +101,7 @@ typedef struct rdg_layout {
  * Score: sigmoid evaluated in fp64 and rounded once to fp32 (a fixed
  * evaluation, bit-identical wherever it is implemented); group score: fp32
  * sum of the group's two largest scores; ties go to the lower index.
- * Limits: N <= 1024, n_group <= 64.  B = 0 is a no-op. */
+ * Limits: N <= 1024.  B = 0 is a no-op. */
 int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
               int32_t* topk_ids, float* topk_w, rdg_stream_t stream);
 
@@ -161,9 +161,10 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  *   y         [m_cap, H] fp32 (RDG_F32) or bf16
  *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype))] int32, zeroed by the
  *             caller (rdg_fill_i32) before this call: after the down GEMM
- *             has stored a row tile's outputs for one column block it adds 1
- *             to that tile's counter with release ordering at device scope;
- *             a tile is complete at rdg_signal_threshold(H, dtype).
+ *             has stored a row tile's outputs for a block of columns it adds
+ *             the block's column count to that tile's counter with release
+ *             ordering at device scope; a tile is complete when its counter
+ *             reaches rdg_signal_threshold(H, dtype) = H.
  * Rows outside [offsets[e], offsets[e] + masked_m[e]) are neither read nor
  * written.  H and I must be multiples of 128. */
 int rdg_grouped_ffn(const rdg_layout* L, int dtype, int H, int I, const void* x_perm, const float* x_perm_scales,

@@ -10,9 +10,10 @@
 //
 //   out[t] = shared_out[t] + sum_{k: pos[t,k] >= 0} w[t,k] * y[pos[t,k]]
 //
-// Design for CDNA4: one wave per token; each lane owns 8 consecutive
-// features per step (a 16-byte bf16 vector), gathers the K expert rows for
-// them, accumulates in fp32 and writes once.  In the polling form, lane 0
+// Design for CDNA4: one wave per (token, 512-feature slice); each lane owns
+// 8 consecutive features (a 16-byte bf16 vector), gathers the K expert rows
+// for them, accumulates in fp32 and writes once.  Slicing the row keeps a
+// 128-token decode batch from occupying only a handful of CUs.  In the polling form, lane 0
 // waits (acquire, device scope) on the counter of each row tile the token
 // reads; a bounded wait turns a tile that never completes into a status
 // code instead of a hang.
@@ -71,9 +72,14 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
                                                  const void* __restrict__ shared_out, void* __restrict__ out,
                                                  const int32_t* signals, int rows_per_sig, int threshold,
                                                  uint64_t timeout_ticks, int32_t* status) {
+    __shared__ int pos_lds[4][32];
+    __shared__ float w_lds[4][32];
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int nvec = H / 8;
-    for (int t = blockIdx.x * 4 + wv; t < T; t += gridDim.x * 4) {
+    const int n_slices = (nvec + kWave - 1) / kWave;
+    const int64_t n_units = (int64_t)T * n_slices;
+    for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += (int64_t)gridDim.x * 4) {
+        const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
         int p = -1;
         float wt = 0.0f;
         if (lane < K) {
@@ -94,11 +100,23 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
             }
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         }
-        for (int v = lane; v < nvec; v += kWave) {
+        // the feature loop below may leave lanes idle: read the slots from LDS
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < K) {
+            pos_lds[wv][lane] = p;
+            w_lds[wv][lane] = wt;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const int v = slice * kWave + lane;
+        if (v < nvec) {
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
             for (int k = 0; k < K; ++k) {
-                const int pk = __shfl(p, k);
-                const float wk = __shfl(wt, k);
+                const int pk = pos_lds[wv][k];
+                const float wk = w_lds[wv][k];
                 if (pk < 0) continue;
                 float yv[8];
                 load8<YDT>(y, (size_t)pk, H, v, yv);
@@ -122,10 +140,11 @@ hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const flo
                           const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
                           int threshold, uint64_t timeout_ticks, int max_blocks, int32_t* status, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    int blocks = (T + 3) / 4;
+    const int64_t units = (int64_t)T * ((H / 8 + kWave - 1) / kWave);
+    int64_t blocks = (units + 3) / 4;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
 #define RDG_COMBINE(YD, OD)                                                                                     \
-    k_combine<YD, OD><<<blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, signals, rows_per_sig,        \
+    k_combine<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, signals, rows_per_sig,        \
                                               threshold, timeout_ticks, status)
     if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_COMBINE(RDG_BF16, RDG_BF16);
     else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_COMBINE(RDG_BF16, RDG_F32);

@@ -18,8 +18,10 @@
 //   2. scan:    one workgroup turns the chunk histograms into per-chunk bases,
 //               counts, padded offsets, masked_m, capacity status and the row
 //               tile tables used by the grouped GEMM.
-//   3. scatter: one wave per token computes its K destinations and copies the
-//               token's row once from HBM into each of them (16-byte vectors).
+//   3. scatter: one wave per (token, 1 KiB slice of its row) computes the K
+//               destinations and copies the slice once from HBM into each of
+//               them (16-byte vectors); slicing keeps small batches from
+//               leaving most CUs idle.
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -151,7 +153,18 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
     const bool act = e < n_local;
     int run = 0;
     if (act) {
-        for (int c = 0; c < n_chunks; ++c) {
+        int c = 0;
+        for (; c + 8 <= n_chunks; c += 8) {  // issue eight independent loads, then scan them
+            int v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = chunk_counts[(size_t)(c + j) * n_local + e];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                chunk_counts[(size_t)(c + j) * n_local + e] = run;
+                run += v[j];
+            }
+        }
+        for (; c < n_chunks; ++c) {
             int32_t* p = chunk_counts + (size_t)c * n_local + e;
             int v = *p;
             *p = run;
@@ -189,9 +202,11 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
     }
 }
 
-// Pass 3.  One wave per token.  row_bytes: bytes of one x row (a multiple of 16).
+// Pass 3.  One wave per (token, 64-vector slice of its row): the slice-0
+// wave also publishes pos and row_src.  row_bytes: bytes of one x row (a
+// multiple of 16); n_slices = ceil(row_bytes / 1024).
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, const float* __restrict__ x_s,
-                                                 int row_bytes, int n_scales, int T, int K,
+                                                 int row_bytes, int n_scales, int n_slices, int T, int K,
                                                  const int32_t* __restrict__ ids, int n_local, int chunk,
                                                  const int32_t* __restrict__ chunk_base,
                                                  const int32_t* __restrict__ tmp_rank,
@@ -199,9 +214,11 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
                                                  const int32_t* __restrict__ masked_m, int32_t* __restrict__ pos,
                                                  int32_t* __restrict__ row_src, uint8_t* __restrict__ x_perm,
                                                  float* __restrict__ x_perm_s) {
+    __shared__ int dst_lds[4][32];
     const int wv = threadIdx.x / kWave, lane = lane_id();
-    const int t = blockIdx.x * 4 + wv;
-    if (t >= T) return;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + wv;
+    if (unit >= (int64_t)T * n_slices) return;
+    const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
     int p = -1;
     if (lane < K) {
         const int64_t i = (int64_t)t * K + lane;
@@ -210,23 +227,32 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
             const int r = chunk_base[(size_t)(i / chunk) * n_local + e] + tmp_rank[i];
             if (r < masked_m[e]) p = offsets[e] + r;
         }
-        pos[i] = p;
-        if (p >= 0) row_src[p] = (int32_t)i;
+        if (slice == 0) {
+            pos[i] = p;
+            if (p >= 0) row_src[p] = (int32_t)i;
+        }
+        dst_lds[wv][lane] = p;
     }
+    // the copy loops below leave lanes idle, so the destinations are read
+    // from the wave's LDS slice rather than shuffled from other lanes
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int* dst = dst_lds[wv];
     const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * row_bytes);
-    const int nvec = row_bytes / 16;
-    for (int v = lane; v < nvec; v += kWave) {
+    const int v = slice * kWave + lane;
+    if (v < row_bytes / 16) {
         const uint4 val = src[v];
         for (int k = 0; k < K; ++k) {
-            const int pk = __shfl(p, k);
+            const int pk = dst[k];
             if (pk >= 0) reinterpret_cast<uint4*>(x_perm + (size_t)pk * row_bytes)[v] = val;
         }
     }
-    if (x_s != nullptr) {
+    if (x_s != nullptr && slice == 0) {
         for (int j = lane; j < n_scales; j += kWave) {
             const float sv = x_s[(size_t)t * n_scales + j];
             for (int k = 0; k < K; ++k) {
-                const int pk = __shfl(p, k);
+                const int pk = dst[k];
                 if (pk >= 0) x_perm_s[(size_t)pk * n_scales + j] = sv;
             }
         }
@@ -297,9 +323,12 @@ hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, 
     err = hipGetLastError();
     if (err != hipSuccess || T == 0) return err;
     const int n_scales = x_scales ? H / 128 : 0;
-    k_scatter<<<(T + 3) / 4, 256, 0, s>>>(static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales, T, K, ids,
-                                          L.n_local, chunk, chunk_counts, tmp_rank, L.offsets, L.masked_m, L.pos,
-                                          L.row_src, static_cast<uint8_t*>(x_perm), x_perm_scales);
+    const int n_slices = (row_bytes + 16 * kWave - 1) / (16 * kWave);
+    const int64_t units = (int64_t)T * n_slices;
+    k_scatter<<<(unsigned)((units + 3) / 4), 256, 0, s>>>(static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales,
+                                                          n_slices, T, K, ids, L.n_local, chunk, chunk_counts,
+                                                          tmp_rank, L.offsets, L.masked_m, L.pos, L.row_src,
+                                                          static_cast<uint8_t*>(x_perm), x_perm_scales);
     return hipGetLastError();
 }
 

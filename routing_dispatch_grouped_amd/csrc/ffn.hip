@@ -280,7 +280,151 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
         __threadfence();
         __syncthreads();
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / BT, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(a.signals + row0 / BT, 128, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Skinny variant for row tiles of at most 16 rows (decode: a few tokens per
+// expert).  Each workgroup owns 16*FPW weight rows of one expert; its four
+// waves split the reduction dimension in four contiguous ranges of 128-wide
+// blocks, and the partial sums are added in LDS in wave order (so the result
+// does not depend on timing).  Many short workgroups instead of few long
+// ones keep the last round of the grid from idling most of the GPU.  Used for
+// every type except the fp8 gate/up stage, whose 1x128 re-quantisation of h
+// needs 128 columns in one workgroup.
+template <int DT, bool GATED, bool SIGNAL, int FPW>
+__global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
+    using M = Mma<DT>;
+    using op_t = typename M::op_t;
+    constexpr int KS = M::KS, U = M::U, ESZ = M::ESZ;
+    constexpr int G = GATED ? 2 : 1;
+    constexpr int OUT_KIND = DT == RDG_F32 ? 0 : 1;
+    __shared__ f32x4_t part[4][FPW * G][kWave];
+
+    const int tile = blockIdx.x;
+    const int n_tiles = a.tile_off[a.n_local];
+    if (tile >= n_tiles) return;  // workgroup-uniform
+    int lo = 0, hi = a.n_local;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (a.tile_off[mid] <= tile) lo = mid;
+        else hi = mid;
+    }
+    const int e = lo;
+    const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * 16;
+    const int row_end = a.offsets[e] + a.masked_m[e];
+    const int f0 = blockIdx.y * (16 * FPW);
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    const size_t wstride = (size_t)a.Kdim * ESZ;
+
+    const uint8_t* arow[FPW];
+    const uint8_t* brow[FPW];
+#pragma unroll
+    for (int rt = 0; rt < FPW; ++rt) {
+        const size_t r = (size_t)e * a.Nout + f0 + rt * 16 + (lane & 15);
+        arow[rt] = a.Wa + r * wstride;
+        brow[rt] = GATED ? a.Wb + r * wstride : nullptr;
+    }
+    const int xr = row0 + (lane & 15);
+    const bool xv = xr < row_end;
+    const uint8_t* xrow = a.X + (size_t)(xv ? xr : row0) * wstride;
+
+    f32x4_t accA[FPW], accB[FPW];
+#pragma unroll
+    for (int rt = 0; rt < FPW; ++rt) {
+        accA[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        accB[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    const int nkb = a.Kdim / 128;
+    const int kb0 = (wv * nkb) / 4, kb1 = ((wv + 1) * nkb) / 4;
+    const float* was = nullptr;
+    const float* wbs = nullptr;
+    if (DT == RDG_FP8_E4M3) {
+        was = a.Was + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
+        if (GATED) wbs = a.Wbs + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
+    }
+    for (int kb = kb0; kb < kb1; ++kb) {
+        if (DT != RDG_FP8_E4M3) {
+#pragma unroll
+            for (int k0 = kb * 128; k0 < kb * 128 + 128; k0 += KS * U) {
+                op_t ra[U][FPW], rb[U][FPW], rx[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+#pragma unroll
+                    for (int rt = 0; rt < FPW; ++rt) {
+                        ra[u][rt] = M::load(arow[rt], k0 + u * KS, lane);
+                        if (GATED) rb[u][rt] = M::load(brow[rt], k0 + u * KS, lane);
+                    }
+                    rx[u] = xv ? M::load(xrow, k0 + u * KS, lane) : M::zero();
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+#pragma unroll
+                    for (int rt = 0; rt < FPW; ++rt) {
+                        accA[rt] = M::mma(accA[rt], ra[u][rt], rx[u]);
+                        if (GATED) accB[rt] = M::mma(accB[rt], rb[u][rt], rx[u]);
+                    }
+            }
+        } else {
+            op_t ra[FPW], rb[FPW];
+#pragma unroll
+            for (int rt = 0; rt < FPW; ++rt) {
+                ra[rt] = M::load(arow[rt], kb * 128, lane);
+                if (GATED) rb[rt] = M::load(brow[rt], kb * 128, lane);
+            }
+            const op_t rx = xv ? M::load(xrow, kb * 128, lane) : M::zero();
+            const float sx = xv ? a.Xs[(size_t)xr * nkb + kb] : 0.0f;
+            const float fa = sx * was[kb], fb = GATED ? sx * wbs[kb] : 0.0f;
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int rt = 0; rt < FPW; ++rt) {
+                accA[rt] += M::mma(z, ra[rt], rx) * fa;
+                if (GATED) accB[rt] += M::mma(z, rb[rt], rx) * fb;
+            }
+        }
+    }
+    // reduce the four K ranges in wave order
+#pragma unroll
+    for (int rt = 0; rt < FPW; ++rt) {
+        part[wv][rt * G][lane] = accA[rt];
+        if (GATED) part[wv][rt * G + 1][lane] = accB[rt];
+    }
+    __syncthreads();
+    if (wv == 0) {
+        const int row = row0 + (lane & 15);
+        const int fl = f0 + (lane >> 4) * 4;
+#pragma unroll
+        for (int rt = 0; rt < FPW; ++rt) {
+            f32x4_t g = part[0][rt * G][lane];
+            f32x4_t u = GATED ? part[0][rt * G + 1][lane] : g;
+#pragma unroll
+            for (int w = 1; w < 4; ++w) {
+                g += part[w][rt * G][lane];
+                if (GATED) u += part[w][rt * G + 1][lane];
+            }
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) v[r] = GATED ? g[r] / (1.0f + __expf(-g[r])) * u[r] : g[r];
+            if (row < row_end) {
+                const size_t idx = (size_t)row * a.Nout + fl + rt * 16;
+                if (OUT_KIND == 0) {
+                    *reinterpret_cast<float4*>(a.O + idx * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                } else {
+                    uint2 o;
+                    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
+                    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
+                    *reinterpret_cast<uint2*>(a.O + idx * 2) = o;
+                }
+            }
+        }
+    }
+    if (SIGNAL) {
+        __threadfence();
+        __syncthreads();
+        if (threadIdx.x == 0)
+            __hip_atomic_fetch_add(a.signals + row0 / 16, 16 * FPW, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -307,9 +451,15 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     g.signals = nullptr;
     (void)ESZ;
     dim3 block(256);
+    constexpr bool kSkinny = BT == 16;
     if (c.stages & 1) {
-        dim3 grid1(c.n_tiles_max, c.I / 128);
-        k_ffn<DT, BT, true, false><<<grid1, block, 0, s>>>(g);
+        if (kSkinny && DT != RDG_FP8_E4M3) {
+            dim3 grid1(c.n_tiles_max, c.I / 16);
+            k_ffn_skinny<DT, true, false, 1><<<grid1, block, 0, s>>>(g);
+        } else {
+            dim3 grid1(c.n_tiles_max, c.I / 128);
+            k_ffn<DT, BT, true, false><<<grid1, block, 0, s>>>(g);
+        }
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -332,11 +482,19 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     d.Os = nullptr;
     d.signals = c.signals;
     (void)hsz;
-    dim3 grid2(c.n_tiles_max, c.H / 128);
-    if (c.signals)
-        k_ffn<DT, BT, false, true><<<grid2, block, 0, s>>>(d);
-    else
-        k_ffn<DT, BT, false, false><<<grid2, block, 0, s>>>(d);
+    if (kSkinny) {
+        dim3 grid2(c.n_tiles_max, c.H / 32);
+        if (c.signals)
+            k_ffn_skinny<DT, false, true, 2><<<grid2, block, 0, s>>>(d);
+        else
+            k_ffn_skinny<DT, false, false, 2><<<grid2, block, 0, s>>>(d);
+    } else {
+        dim3 grid2(c.n_tiles_max, c.H / 128);
+        if (c.signals)
+            k_ffn<DT, BT, false, true><<<grid2, block, 0, s>>>(d);
+        else
+            k_ffn<DT, BT, false, false><<<grid2, block, 0, s>>>(d);
+    }
     return hipGetLastError();
 }
 

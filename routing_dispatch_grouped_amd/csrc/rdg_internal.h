@@ -94,9 +94,11 @@ __host__ __device__ inline size_t ws_tile_off_bytes(int n_local) {
 __host__ __device__ inline size_t ws_chunk_bytes(int n_local) {
     return align256(sizeof(int32_t) * kMaxChunks * (size_t)n_local);
 }
+// Entries per counting-sort chunk: at most kMaxChunks chunks, and at least
+// four 64-entry pieces per chunk so small dispatches scan few chunks.
 __host__ __device__ inline int chunk_size_for(int64_t n_rows) {
     int64_t pieces = (n_rows + (int64_t)kWave * kMaxChunks - 1) / ((int64_t)kWave * kMaxChunks);
-    if (pieces < 1) pieces = 1;
+    if (pieces < 4) pieces = 4;
     return (int)(pieces * kWave);
 }
 __host__ __device__ inline int bt_index(int bt) { return bt == 16 ? 0 : bt == 32 ? 1 : bt == 64 ? 2 : 3; }

@@ -10,7 +10,7 @@
 //
 // Design for CDNA4: a token's N <= 1024 scores sit in LDS (one wave's
 // private slice) and in registers (N/64 per lane, expert e on lane e % 64).
-// Group scores are computed by the first n_group lanes; each of the
+// Group g's score is computed by lane g % 64; each of the
 // topk_group + K selection rounds is one 64-lane max-reduction of a 64-bit
 // key (score bits << 32 | ~index) -- the positive fp32 scores order like
 // their bit patterns, and ~index makes the lower index win a tie.
@@ -60,6 +60,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
                                                int topk_group, int K, float scale, int32_t* __restrict__ ids,
                                                float* __restrict__ w) {
     __shared__ float lds[4][64 * VPL];
+    __shared__ uint8_t gsel_lds[4][64 * VPL];
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int t = blockIdx.x * 4 + wv;
     if (t >= B) return;  // the wave is idle; nothing below synchronises across waves
@@ -77,34 +78,50 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-    // group score: sum of the group's two largest scores (with multiplicity)
+    // group score: sum of the group's two largest scores (with multiplicity);
+    // lane l owns groups l, l+64, ... (n_group <= N <= 64*VPL, so VPL slots suffice)
     const int gs = N / n_group;
-    uint64_t gkey = 0;
-    if (lane < n_group) {
-        float a = -1.0f, b = -1.0f;
-        for (int i = lane * gs; i < (lane + 1) * gs; ++i) {
-            float v = s_lds[i];
-            if (v > a) {
-                b = a;
-                a = v;
-            } else if (v > b) {
-                b = v;
+    uint64_t gkey[VPL];
+#pragma unroll
+    for (int j = 0; j < VPL; ++j) {
+        const int g = lane + kWave * j;
+        gkey[j] = 0ull;
+        if (g < n_group) {
+            float a = -1.0f, b = -1.0f;
+            for (int i = g * gs; i < (g + 1) * gs; ++i) {
+                const float v = s_lds[i];
+                if (v > a) {
+                    b = a;
+                    a = v;
+                } else if (v > b) {
+                    b = v;
+                }
             }
+            gkey[j] = make_key(gs >= 2 ? a + b : a, g);
         }
-        gkey = make_key(gs >= 2 ? a + b : a, lane);
     }
-    // keep topk_group groups
-    uint64_t gmask = 0;
+    // keep topk_group groups; the kept set is a byte per group in LDS
+    uint8_t* gsel = gsel_lds[wv];
+    for (int g = lane; g < n_group; g += kWave) gsel[g] = 0;
     for (int r = 0; r < topk_group; ++r) {
-        uint64_t m = wave_max_u64(((gmask >> lane) & 1ull) ? 0ull : gkey);
-        gmask |= 1ull << key_index(m);
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < VPL; ++j) best = gkey[j] > best ? gkey[j] : best;
+        const int g = key_index(wave_max_u64(best));
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (lane + kWave * j == g) gkey[j] = 0ull;
+        if (lane == 0) gsel[g] = 1;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // top-K experts of the kept groups
     uint64_t key[VPL];
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         int e = lane + kWave * v;
-        bool cand = e < N && ((gmask >> (e / gs)) & 1ull);
+        bool cand = e < N && gsel[e / gs];
         key[v] = cand ? make_key(s[v], e) : 0ull;
     }
     float my_s = 0.0f;

@@ -46,9 +46,18 @@ def test_combine_parity(T, K, E, H, ydt, shared):
     if ydt == "f32":
         assert oracle.rel_err(g, ref) <= 1e-6
     else:
-        # fp32 vs fp64 accumulation may move a value across a bf16 rounding
-        # boundary: at most one bf16 step, and rarely
+        # fp32 (slot order) vs fp64 accumulation: the fp32 sum is within
+        # (K+2) * 2^-24 of the sum of |terms|; rounding both to bf16 can then
+        # land on neighbouring values, one bf16 step (2^-7 relative) apart
         gd, rd = oracle.bf16_decode(g), oracle.bf16_decode(ref)
-        step = np.abs(rd) * 2.0 ** -7 + 1e-30
-        assert np.all(np.abs(gd - rd) <= step)
+        yd = oracle.bf16_decode(np_of(y_h))
+        pos = ref_l["pos"]
+        mag = np.zeros((T, H))
+        for k in range(K):
+            ok = pos[:, k] >= 0
+            mag[ok] += np.abs(w[ok, k, None].astype(np.float64) * yd[pos[ok, k]])
+        if sh_h is not None:
+            mag += np.abs(oracle.bf16_decode(np_of(sh_h)))
+        bound = np.maximum(np.abs(rd), np.abs(gd)) * 2.0 ** -7 + mag * (K + 2) * 2.0 ** -24 + 1e-30
+        assert np.all(np.abs(gd - rd) <= bound)
         assert np.mean(g != ref) < 1e-3

@@ -29,8 +29,10 @@ def _check(logits_np, n_group, topk_group, K, scale=1.0):
     ri, rw = oracle.route(logits_np, n_group, topk_group, K, scale)
     bad = np.flatnonzero((gi != ri).any(1))
     assert len(bad) == 0, ("ids differ at tokens", bad[:10], gi[bad[:3]], ri[bad[:3]])
-    # fp32 s/sum*scale vs the fp64 value rounded once: a few ulp
-    assert np.max(np.abs(gw.astype(np.float64) - rw) / np.maximum(np.abs(rw), 1e-30)) <= 4e-7
+    # the kernel sums K fp32 scores in slot order, then divides and scales in
+    # fp32; the oracle rounds the fp64 value once: within (K + 2) fp32 ulps
+    bound = (K + 2) * 2.0 ** -24
+    assert np.max(np.abs(gw.astype(np.float64) - rw) / np.maximum(np.abs(rw), 1e-30)) <= bound
 
 
 @pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16"])
