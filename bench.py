@@ -58,15 +58,19 @@ def main():
     logits_np = synth.logits(cfg)
     logits = torch.from_numpy(logits_np).to(dev)
     x = synth.x(cfg, B, device=dev)
+    # weights are packed once into the grouped GEMMs' tile order (load time, not timed)
     W1 = torch.empty((N, I, H), dtype=torch.bfloat16, device=dev)
     W3 = torch.empty((N, I, H), dtype=torch.bfloat16, device=dev)
     W2 = torch.empty((N, H, I), dtype=torch.bfloat16, device=dev)
     for e in range(N):
         w = synth.expert_weights(cfg, e, device=dev)
-        W1[e].copy_(w["W1"]); W3[e].copy_(w["W3"]); W2[e].copy_(w["W2"])
+        rdg.rdg_pack_weights(w["W1"], DT, W1[e]); rdg.rdg_pack_weights(w["W3"], DT, W3[e])
+        rdg.rdg_pack_weights(w["W2"], DT, W2[e])
         del w
     sh = synth.expert_weights(cfg, 0, device=dev, shared=True)
-    sW1, sW3, sW2 = (sh[k].unsqueeze(0).contiguous() for k in ("W1", "W3", "W2"))
+    sW1, sW3, sW2 = (torch.empty_like(sh[k]).unsqueeze(0) for k in ("W1", "W3", "W2"))
+    for k, dst in (("W1", sW1), ("W3", sW3), ("W2", sW2)):
+        rdg.rdg_pack_weights(sh[k], DT, dst[0])
 
     # ---------------------------------------------------------------- buffers
     ids = torch.empty((B, K), dtype=torch.int32, device=dev)
@@ -143,11 +147,11 @@ def main():
     }
 
     if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, logits_np, x, W1, W3, W2, sh)
+        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, logits_np, x, sh, dev)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, n_tok, logits_np, x, W1, W3, W2, sh):
+def cpu_baseline(cfg, n_tok, logits_np, x, sh, dev):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     routing of the whole batch and the layer output of the first n_tok tokens.
     Host copies of the needed inputs are made before the clock starts."""
@@ -162,7 +166,9 @@ def cpu_baseline(cfg, n_tok, logits_np, x, W1, W3, W2, sh):
     ri, rw = oracle.route(logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
     sel = np.arange(n_tok, dtype=np.int32)
     used = set(np.unique(ri[sel]).tolist())
-    experts = [dict(W1=u16(W1[e]), W3=u16(W3[e]), W2=u16(W2[e])) if e in used else None for e in range(cfg["N"])]
+    import synth
+    experts = [{k: u16(v) for k, v in synth.expert_weights(cfg, e, device=dev).items()} if e in used else None
+               for e in range(cfg["N"])]
     shared = {k: u16(v) for k, v in sh.items()}
     xh = u16(x)
     t0 = time.perf_counter()

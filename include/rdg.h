@@ -150,7 +150,8 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  * sections 2-3).  For every valid row r of expert e:
  *   h[r] = silu(x[r] W1_e^T) * (x[r] W3_e^T)      (stored in h_ws)
  *   y[r] = h[r] W2_e^T                             (stored in y)
- * Weights are K-major: W1, W3 [n_local, I, H]; W2 [n_local, H, I].
+ * Weights: W1, W3 hold [n_local, I, H] and W2 [n_local, H, I], each packed
+ * by rdg_pack_weights (n_mat = n_local).
  * dtype RDG_F32: everything fp32.  RDG_BF16: bf16 operands, fp32
  * accumulation, h and y bf16.  RDG_FP8_E4M3: e4m3 operands, x_perm_scales
  * [m_cap, H/128], weight scales W1_s, W3_s [n_local, I/128, H/128] and
@@ -171,6 +172,20 @@ int rdg_grouped_ffn(const rdg_layout* L, int dtype, int H, int I, const void* x_
                     const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
                     const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,
                     rdg_stream_t stream);
+
+/* Weight packing, done once when weights are loaded.  The grouped GEMMs
+ * read every weight matrix in a tiled order in which each 16-row x KS tile
+ * (KS = 4 fp32, 32 bf16, 128 fp8 elements of the reduction dimension) is
+ * stored contiguously in the order the 64 lanes of a wavefront consume it
+ * as an MFMA operand, so that each load instruction fetches one contiguous
+ * KiB (fp8: the tile is two such KiB halves).  Tiles are ordered by matrix,
+ * then by 16-row group, then along the reduction dimension.
+ *   W         [n_mat, rows, cols] row-major (cols = the reduction dimension)
+ *   W_packed  the same number of bytes, packed
+ * rows must be a multiple of 16 and cols of 128.  The block scales of fp8
+ * weights are not packed. */
+size_t rdg_packed_weight_bytes(int dtype, int n_mat, int rows, int cols);
+int rdg_pack_weights(const void* W, int dtype, int n_mat, int rows, int cols, void* W_packed, rdg_stream_t stream);
 
 /* The two stages of rdg_grouped_ffn as separate launches (same arguments
  * and rules): the gate/up GEMM with the SiLU-gated product writing h (and

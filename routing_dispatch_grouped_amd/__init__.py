@@ -52,6 +52,8 @@ _SIGS = {
     "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I64, _I, _P], _I),
     "rdg_quantize_fp8": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "rdg_fill_i32": ([_P, ctypes.c_int32, _I64, _P], _I),
+    "rdg_packed_weight_bytes": ([_I, _I, _I, _I], _SZ),
+    "rdg_pack_weights": ([_P, _I, _I, _I, _I, _P, _P], _I),
     "rdg_check_status": ([_P, _P, _P], _I),
     "rdg_strerror": ([_I], ctypes.c_char_p),
     "rdg_version": ([], _I),
@@ -189,6 +191,14 @@ def rdg_quantize_fp8(src, src_dtype, block_rows, q, scales, stream=None):
     rows, cols = src.shape
     _check(_lib.rdg_quantize_fp8(_ptr(src), src_dtype, rows, cols, block_rows, _ptr(q), _ptr(scales),
                                  _stream(stream)), "rdg_quantize_fp8")
+
+
+def rdg_pack_weights(W, dtype, W_packed, stream=None):
+    """W: [n_mat, rows, cols] (or [rows, cols]) device tensor; W_packed: same byte size."""
+    shape = tuple(W.shape)
+    n_mat, rows, cols = (1,) + shape if len(shape) == 2 else shape
+    _check(_lib.rdg_pack_weights(_ptr(W), dtype, n_mat, rows, cols, _ptr(W_packed), _stream(stream)),
+           "rdg_pack_weights")
 
 
 def rdg_fill_i32(p, value, stream=None):

@@ -227,6 +227,21 @@ int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int blo
     return hip_rc(launch_quantize(src, src_dtype, rows, cols, block_rows, q, scales, stream));
 }
 
+size_t rdg_packed_weight_bytes(int dtype, int n_mat, int rows, int cols) {
+    if (n_mat < 0 || rows < 0 || cols < 0) return 0;
+    const size_t esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2 : dtype == RDG_FP8_E4M3 ? 1 : 0;
+    return esz * (size_t)n_mat * rows * cols;
+}
+
+int rdg_pack_weights(const void* W, int dtype, int n_mat, int rows, int cols, void* W_packed, rdg_stream_t stream) {
+    if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3) return RDG_EINVAL;
+    if (n_mat < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return RDG_EINVAL;
+    if ((size_t)n_mat * rows * cols > 0 && (!W || !W_packed || !aligned16(W) || !aligned16(W_packed)))
+        return RDG_EINVAL;
+    if (W == W_packed) return RDG_EINVAL;
+    return hip_rc(launch_pack(W, dtype, n_mat, rows, cols, W_packed, stream));
+}
+
 int rdg_fill_i32(int32_t* p, int32_t value, int64_t n, rdg_stream_t stream) {
     if (n < 0 || (n > 0 && !p)) return RDG_EINVAL;
     return hip_rc(launch_fill_i32(p, value, n, stream));

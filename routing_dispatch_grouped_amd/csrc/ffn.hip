@@ -14,10 +14,12 @@
 // (BT rows of one expert) times 128 output columns; wave w owns columns
 // [32w, 32w + 32) as two 16-row MFMA tiles, so the weight rows it streams
 // are read exactly once per row tile, straight from HBM into registers (no
-// LDS: nothing else in the workgroup reuses them).  The token rows are the
-// MFMA's second operand, BT/16 column tiles, shared by the four waves
-// through L2.  Both operands are K-major, so each lane's MFMA operand is one
-// contiguous 16- or 32-byte load.  MFMA: 16x16x4 f32, 16x16x32 bf16, and
+// LDS: nothing else in the workgroup reuses them).  Weights arrive packed
+// (pack.hip): each MFMA operand tile is one contiguous KiB in lane order, so
+// every weight load instruction is a fully contiguous KiB, which HBM serves
+// far better than 64-byte pieces of 16 different rows.  The token rows are
+// the MFMA's second operand, BT/16 column tiles, shared by the four waves
+// through L2, loaded from their natural K-major rows.  MFMA: 16x16x4 f32, 16x16x32 bf16, and
 // 16x16x128 fp8 e4m3 (one instruction per 128-long scale block, then the
 // partial sum is promoted into the fp32 accumulator with its activation and
 // weight block scales).  The row-tile -> expert mapping comes from the prefix
@@ -30,10 +32,16 @@ namespace {
 template <int DT>
 struct Mma;
 
+// Per type: the MFMA step KS (reduction elements), element size, unroll U,
+// the packed weight tile size BLK (see pack.hip), and operand loads from a
+// natural K-major row (tokens) or from a packed weight tile.
 template <>
 struct Mma<RDG_F32> {
     using op_t = float;
-    static constexpr int KS = 4, ESZ = 4, U = 8;
+    static constexpr int KS = 4, ESZ = 4, U = 8, BLK = 256;
+    __device__ static op_t load_tile(const uint8_t* tile, int lane) {
+        return reinterpret_cast<const float*>(tile)[lane];
+    }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
         return reinterpret_cast<const float*>(row)[k0 + (lane >> 4)];
     }
@@ -46,7 +54,10 @@ struct Mma<RDG_F32> {
 template <>
 struct Mma<RDG_BF16> {
     using op_t = bf16x8_t;
-    static constexpr int KS = 32, ESZ = 2, U = 4;
+    static constexpr int KS = 32, ESZ = 2, U = 4, BLK = 1024;
+    __device__ static op_t load_tile(const uint8_t* tile, int lane) {
+        return *reinterpret_cast<const bf16x8_t*>(tile + lane * 16);
+    }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
         return *reinterpret_cast<const bf16x8_t*>(row + (size_t)(k0 + (lane >> 4) * 8) * 2);
     }
@@ -59,7 +70,15 @@ struct Mma<RDG_BF16> {
 template <>
 struct Mma<RDG_FP8_E4M3> {
     using op_t = i32x8_t;
-    static constexpr int KS = 128, ESZ = 1, U = 1;
+    static constexpr int KS = 128, ESZ = 1, U = 1, BLK = 2048;
+    __device__ static op_t load_tile(const uint8_t* tile, int lane) {
+        const uint4 a = *reinterpret_cast<const uint4*>(tile + lane * 16);
+        const uint4 b = *reinterpret_cast<const uint4*>(tile + 1024 + lane * 16);
+        op_t r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+        return r;
+    }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
         const uint4* p = reinterpret_cast<const uint4*>(row + k0 + (lane >> 4) * 32);
         uint4 a = p[0], b = p[1];
@@ -117,13 +136,15 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
     const int fw = f0 + wv * 32;
     const size_t wstride = (size_t)a.Kdim * ESZ;
 
+    // packed weights: the tiles of one 16-row group are contiguous along K
+    const int nks = a.Kdim / KS;
     const uint8_t* arow[2];
     const uint8_t* brow[2];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
-        const size_t r = (size_t)e * a.Nout + fw + rt * 16 + (lane & 15);
-        arow[rt] = a.Wa + r * wstride;
-        brow[rt] = GATED ? a.Wb + r * wstride : nullptr;
+        const size_t grp = (size_t)e * (a.Nout / 16) + (fw + rt * 16) / 16;
+        arow[rt] = a.Wa + grp * nks * M::BLK;
+        brow[rt] = GATED ? a.Wb + grp * nks * M::BLK : nullptr;
     }
     const uint8_t* xrow[NCT];
     bool xv[NCT];
@@ -157,8 +178,9 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
         for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                ra[u][rt] = M::load(arow[rt], k0 + u * KS, lane);
-                if (GATED) rb[u][rt] = M::load(brow[rt], k0 + u * KS, lane);
+                const size_t t_off = (size_t)(k0 / KS + u) * M::BLK;
+                ra[u][rt] = M::load_tile(arow[rt] + t_off, lane);
+                if (GATED) rb[u][rt] = M::load_tile(brow[rt] + t_off, lane);
             }
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) rx[u][ct] = xv[ct] ? M::load(xrow[ct], k0 + u * KS, lane) : M::zero();
@@ -319,13 +341,14 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const size_t wstride = (size_t)a.Kdim * ESZ;
 
+    const int nks = a.Kdim / KS;
     const uint8_t* arow[FPW];
     const uint8_t* brow[FPW];
 #pragma unroll
     for (int rt = 0; rt < FPW; ++rt) {
-        const size_t r = (size_t)e * a.Nout + f0 + rt * 16 + (lane & 15);
-        arow[rt] = a.Wa + r * wstride;
-        brow[rt] = GATED ? a.Wb + r * wstride : nullptr;
+        const size_t grp = (size_t)e * (a.Nout / 16) + (f0 + rt * 16) / 16;
+        arow[rt] = a.Wa + grp * nks * M::BLK;
+        brow[rt] = GATED ? a.Wb + grp * nks * M::BLK : nullptr;
     }
     const int xr = row0 + (lane & 15);
     const bool xv = xr < row_end;
@@ -354,8 +377,9 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int rt = 0; rt < FPW; ++rt) {
-                        ra[u][rt] = M::load(arow[rt], k0 + u * KS, lane);
-                        if (GATED) rb[u][rt] = M::load(brow[rt], k0 + u * KS, lane);
+                        const size_t t_off = (size_t)(k0 / KS + u) * M::BLK;
+                        ra[u][rt] = M::load_tile(arow[rt] + t_off, lane);
+                        if (GATED) rb[u][rt] = M::load_tile(brow[rt] + t_off, lane);
                     }
                     rx[u] = xv ? M::load(xrow, k0 + u * KS, lane) : M::zero();
                 }
@@ -371,8 +395,8 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
             op_t ra[FPW], rb[FPW];
 #pragma unroll
             for (int rt = 0; rt < FPW; ++rt) {
-                ra[rt] = M::load(arow[rt], kb * 128, lane);
-                if (GATED) rb[rt] = M::load(brow[rt], kb * 128, lane);
+                ra[rt] = M::load_tile(arow[rt] + (size_t)kb * M::BLK, lane);
+                if (GATED) rb[rt] = M::load_tile(brow[rt] + (size_t)kb * M::BLK, lane);
             }
             const op_t rx = xv ? M::load(xrow, kb * 128, lane) : M::zero();
             const float sx = xv ? a.Xs[(size_t)xr * nkb + kb] : 0.0f;
@@ -427,6 +451,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
             __hip_atomic_fetch_add(a.signals + row0 / 16, 16 * FPW, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
+
 
 template <int DT, int BT>
 hipError_t launch_bt(const FfnCall& c, hipStream_t s) {

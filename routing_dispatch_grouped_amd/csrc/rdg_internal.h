@@ -115,6 +115,7 @@ hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, 
                            int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s);
 hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+hipError_t launch_pack(const void* W, int dtype, int n_mat, int rows, int cols, void* P, hipStream_t s);
 hipError_t launch_quantize(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
                            float* scales, hipStream_t s);
 

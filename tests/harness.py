@@ -40,11 +40,13 @@ def torch_dtype(dt):
 
 
 class ExpertSet:
-    """Stacked device weights of n experts ([n, I, H], [n, I, H], [n, H, I]).
+    """Stacked device weights of n experts, packed for the grouped GEMMs
+    (rdg_pack_weights) from natural [n, I, H], [n, I, H], [n, H, I] weights.
 
-    fp32/bf16 workloads store them as generated.  fp8 workloads generate fp32
-    weights, quantise them on the device with rdg_quantize_fp8, and keep the
-    fp32 originals' seeds so the oracle can quantise its own copy."""
+    fp32/bf16 workloads pack the generated weights.  fp8 workloads quantise
+    the generated fp32 weights on the device (rdg_quantize_fp8, 128x128
+    blocks), keep those natural codes for the bit-exact check against the
+    oracle's own quantisation, and pack them."""
 
     def __init__(self, cfg, expert_ids, device=DEV, shared=False):
         m = rdg()
@@ -55,37 +57,41 @@ class ExpertSet:
         n = len(self.ids)
         self.fp8 = cfg["dtype"] == "fp8"
         sdt = torch.uint8 if self.fp8 else synth.storage_dtype(cfg)
+        code = dt_code(cfg)
         self.W1 = torch.empty((n, I, H), dtype=sdt, device=device)
         self.W3 = torch.empty((n, I, H), dtype=sdt, device=device)
         self.W2 = torch.empty((n, H, I), dtype=sdt, device=device)
         self.s1 = self.s3 = self.s2 = None
+        self.codes = None
         if self.fp8:
             f = dict(dtype=torch.float32, device=device)
             self.s1 = torch.empty((n, I // 128, H // 128), **f)
             self.s3 = torch.empty((n, I // 128, H // 128), **f)
             self.s2 = torch.empty((n, H // 128, I // 128), **f)
+            self.codes = {k: torch.empty_like(v) for k, v in (("W1", self.W1), ("W3", self.W3), ("W2", self.W2))}
         for j, e in enumerate(self.ids):
             w = synth.expert_weights(cfg, e, device=device, shared=shared)
-            if not self.fp8:
-                self.W1[j].copy_(w["W1"]); self.W3[j].copy_(w["W3"]); self.W2[j].copy_(w["W2"])
-            else:
-                for name, dst, sc in (("W1", self.W1, self.s1), ("W3", self.W3, self.s3), ("W2", self.W2, self.s2)):
-                    m.rdg_quantize_fp8(w[name], m.RDG_F32, 128, dst[j], sc[j])
+            for name, dst, sc in (("W1", self.W1, self.s1), ("W3", self.W3, self.s3), ("W2", self.W2, self.s2)):
+                if self.fp8:
+                    nat = self.codes[name][j]
+                    m.rdg_quantize_fp8(w[name], m.RDG_F32, 128, nat, sc[j])
+                else:
+                    nat = w[name]
+                m.rdg_pack_weights(nat, code, dst[j])
             del w
 
     def oracle_expert(self, j, check_codes=True):
-        """Host copy of expert j in the oracle's storage form (fp8: the
-        oracle's own quantisation of the same fp32 weights; optionally check
-        that the device codes match it bit for bit)."""
-        if not self.fp8:
-            return dict(W1=np_of(self.W1[j]), W3=np_of(self.W3[j]), W2=np_of(self.W2[j]))
+        """Expert j for the oracle, in natural layout, straight from the
+        generator (fp8: the oracle's own quantisation of the same fp32
+        weights, optionally checked bit for bit against the device's codes)."""
         w = synth.expert_weights(self.cfg, self.ids[j], device=self.W1.device, shared=self.shared)
+        if not self.fp8:
+            return {k: np_of(v) for k, v in w.items()}
         out = {}
-        for name, dev_q, dev_s, key in (("W1", self.W1, self.s1, "1"), ("W3", self.W3, self.s3, "3"),
-                                        ("W2", self.W2, self.s2, "2")):
+        for name, key, dev_s in (("W1", "1", self.s1), ("W3", "3", self.s3), ("W2", "2", self.s2)):
             q, s = oracle.quantize_fp8(np_of(w[name]), 128)
             if check_codes:
-                assert np.array_equal(q, np_of(dev_q[j])), "device weight codes differ from the oracle's"
+                assert np.array_equal(q, np_of(self.codes[name][j])), "device weight codes differ from the oracle's"
                 assert np.array_equal(s, np_of(dev_s[j])), "device weight scales differ from the oracle's"
             out["W" + key], out["s" + key] = q, s
         return out

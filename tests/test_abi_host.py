@@ -35,7 +35,7 @@ def test_host_queries_and_validation():
     L = rdg._lib
     assert rdg.rdg_version() >= 100
     assert rdg.strerror(rdg.RDG_ECAPACITY).startswith("rows exceed")
-    assert L.rdg_signal_threshold(7168, rdg.RDG_FP8_E4M3) == 56
+    assert L.rdg_signal_threshold(7168, rdg.RDG_FP8_E4M3) == 7168  # counters count finished columns
     assert L.rdg_signal_threshold(100, rdg.RDG_BF16) == rdg.RDG_EINVAL
     # workspace grows with the dispatched entries and the expert count
     a = L.rdg_dispatch_workspace_bytes(128, 8, 256)
@@ -55,3 +55,12 @@ def test_layout_struct_matches_header():
     # 6 int32 fields then 7 pointers
     assert ctypes.sizeof(rdg.rdg_layout) == 6 * 4 + 7 * 8
     assert rdg.rdg_layout.counts.offset == 24
+
+
+def test_pack_validation():
+    import routing_dispatch_grouped_amd as rdg
+    L = rdg._lib
+    assert L.rdg_packed_weight_bytes(rdg.RDG_BF16, 256, 2048, 7168) == 256 * 2048 * 7168 * 2
+    assert L.rdg_pack_weights(None, rdg.RDG_BF16, 1, 20, 128, None, None) == rdg.RDG_EINVAL   # rows % 16
+    assert L.rdg_pack_weights(None, rdg.RDG_BF16, 1, 16, 100, None, None) == rdg.RDG_EINVAL   # cols % 128
+    assert L.rdg_pack_weights(None, 7, 1, 16, 128, None, None) == rdg.RDG_EINVAL              # dtype
