@@ -1,16 +1,22 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: route -> dispatch
--> grouped gate/up GEMM (+SiLU-gated product) -> grouped down GEMM ->
-combine, plus the shared expert, for the DeepSeek-V3-shaped decode layer with
-every expert on this GPU (128 tokens, H=7168, 256 experts in 8 groups of 32,
-4 groups kept, top-8, I=2048, shared expert I=2048, bf16, masked layout with
-256 rows per expert).  Inputs are seeded synthetic tensors already resident
-in HBM.  Prints one JSON line.
+A step is one pass of the whole hot path over one batch of seeded synthetic
+input already resident in HBM.  The default workload (the one the JSON line
+reports) is the DeepSeek-V3-shaped decode layer with every expert on this
+GPU: 128 tokens, H=7168, 256 experts in 8 groups of 32, 4 groups kept,
+top-8, I=2048, shared expert I=2048, bf16, masked layout with 256 rows per
+expert.  Its step: route -> dispatch -> shared expert -> grouped gate/up GEMM
+(+SiLU-gated product) -> grouped down GEMM -> combine.
+
+--workload selects the other layers the parity tests cover (tiny fp32,
+4096-token bf16 prefill, and the fp8 decode / prefill rank shares with EPLB
+remap; the prefill share overlaps its signalled down GEMM and the shared
+expert with a polling combine on a second stream).
 
 Extra fields: "roofline" for the dominant kernel (the grouped gate/up GEMM,
-timed with HIP events on its own stream) and "cpu_baseline" (the CPU oracle
-timed on a bounded sample of the same workload on this host).
+timed with HIP events on the stream it is launched on) and "cpu_baseline"
+(the CPU oracle timed on a bounded sample of the same workload on this host,
+default workload only).
 """
 import argparse
 import json
@@ -23,6 +29,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 
 
 def parse():
@@ -30,9 +37,204 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode_bf16", choices=["decode_bf16"])
+    p.add_argument("--workload", default="decode_bf16",
+                   choices=["decode_bf16", "tiny_fp32", "prefill_bf16", "decode_rank_fp8", "prefill_rank_fp8"])
     p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
     return p.parse_args()
+
+
+class Bench:
+    """Buffers and the step of one workload."""
+
+    def __init__(self, name, dev):
+        import torch
+
+        import routing_dispatch_grouped_amd as rdg
+        import synth
+        self.torch, self.rdg, self.synth = torch, rdg, synth
+        self.name, self.dev = name, dev
+        self.cfg = cfg = synth.WORKLOADS[name]
+        self.DT = {"f32": rdg.RDG_F32, "bf16": rdg.RDG_BF16, "fp8": rdg.RDG_FP8_E4M3}[cfg["dtype"]]
+        self.sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[cfg["dtype"]]
+        self.ydt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
+        self.YDT = rdg.RDG_F32 if cfg["dtype"] == "f32" else rdg.RDG_BF16
+        self.events = []
+        self.stream = torch.cuda.current_stream()
+        self.rank = "B_global" in cfg
+        if self.rank:
+            self._setup_rank()
+        else:
+            self._setup_full()
+
+    # ------------------------------------------------------------ weights
+    def _experts(self, ids, shared=False):
+        """Packed device weights for the listed logical experts (+ fp8 scales)."""
+        torch, rdg, synth, cfg = self.torch, self.rdg, self.synth, self.cfg
+        H = cfg["H"]
+        I = cfg["shared_I"] if shared else cfg["I"]
+        n = len(ids)
+        W = {k: torch.empty(shape, dtype=self.sdt, device=self.dev)
+             for k, shape in (("W1", (n, I, H)), ("W3", (n, I, H)), ("W2", (n, H, I)))}
+        S = {}
+        if self.DT == rdg.RDG_FP8_E4M3:
+            S = {k: torch.empty(shape, dtype=torch.float32, device=self.dev)
+                 for k, shape in (("W1", (n, I // 128, H // 128)), ("W3", (n, I // 128, H // 128)),
+                                  ("W2", (n, H // 128, I // 128)))}
+        for j, e in enumerate(ids):
+            w = synth.expert_weights(cfg, e, device=self.dev, shared=shared)
+            for k in ("W1", "W3", "W2"):
+                src = w[k]
+                if S:
+                    q = torch.empty(src.shape, dtype=torch.uint8, device=self.dev)
+                    rdg.rdg_quantize_fp8(src, rdg.RDG_F32, 128, q, S[k][j])
+                    src = q
+                rdg.rdg_pack_weights(src, self.DT, W[k][j])
+            del w
+        return W, S
+
+    def _quant(self, x):
+        torch, rdg = self.torch, self.rdg
+        q = torch.empty(x.shape, dtype=torch.uint8, device=self.dev)
+        s = torch.empty((x.shape[0], x.shape[1] // 128), dtype=torch.float32, device=self.dev)
+        rdg.rdg_quantize_fp8(x, rdg.RDG_BF16, 1, q, s)
+        return q, s
+
+    def _buffers(self, T, K, n_local, kind, block_m=128, m_max=0):
+        torch, rdg, cfg = self.torch, self.rdg, self.cfg
+        H, I = cfg["H"], cfg["I"]
+        self.L = rdg.Layout(kind, n_local, T, K, self.dev, block_m=block_m, m_max=m_max)
+        m_cap = self.L.m_cap
+        self.x_perm = torch.empty((m_cap, H), dtype=self.sdt, device=self.dev)
+        self.h = torch.empty((m_cap, I), dtype=self.sdt, device=self.dev)
+        self.y = torch.empty((m_cap, H), dtype=self.ydt, device=self.dev)
+        fp8 = self.DT == rdg.RDG_FP8_E4M3
+        self.x_perm_s = torch.empty((m_cap, H // 128), dtype=torch.float32, device=self.dev) if fp8 else None
+        self.h_s = torch.empty((m_cap, I // 128), dtype=torch.float32, device=self.dev) if fp8 else None
+
+    def _shared_buffers(self, T):
+        torch, rdg, cfg = self.torch, self.rdg, self.cfg
+        shI = cfg["shared_I"]
+        self.Ls = rdg.Layout(rdg.RDG_CONTIGUOUS, 1, T, 1, self.dev, block_m=16, m_cap=T)
+        self.hs = torch.empty((T, shI), dtype=self.sdt, device=self.dev)
+        self.hs_s = (torch.empty((T, shI // 128), dtype=torch.float32, device=self.dev)
+                     if self.DT == rdg.RDG_FP8_E4M3 else None)
+        self.ys = torch.empty((T, cfg["H"]), dtype=self.ydt, device=self.dev)
+
+    def _setup_full(self):
+        torch, rdg, synth, cfg = self.torch, self.rdg, self.synth, self.cfg
+        B, N, K = cfg["B"], cfg["N"], cfg["K"]
+        self.T = B
+        self.logits_np = synth.logits(cfg)
+        self.logits = torch.from_numpy(self.logits_np).to(self.dev)
+        self.x = synth.x(cfg, B, device=self.dev)
+        self.W, self.S = self._experts(range(N))
+        self.Wsh, self.Ssh = self._experts([0], shared=True)
+        self.ids = torch.empty((B, K), dtype=torch.int32, device=self.dev)
+        self.tw = torch.empty((B, K), dtype=torch.float32, device=self.dev)
+        kind = rdg.RDG_MASKED if cfg["layout"] == "masked" else rdg.RDG_CONTIGUOUS
+        self._buffers(B, K, N, kind, block_m=128 if kind == rdg.RDG_CONTIGUOUS else 128, m_max=cfg.get("m_max", 0))
+        self._shared_buffers(B)
+        self.out = torch.empty((B, cfg["H"]), dtype=self.ydt, device=self.dev)
+
+    def _setup_rank(self):
+        """One rank's received share: the global batch is routed and remapped on
+        the device once (setup, untimed) to find the rows this rank receives."""
+        torch, rdg, synth, cfg = self.torch, self.rdg, self.synth, self.cfg
+        import numpy as np
+        K = cfg["K"]
+        plan = synth.eplb_plan(cfg)
+        self.plan = plan
+        lg = torch.from_numpy(synth.logits(cfg)).to(self.dev)
+        Tg = lg.shape[0]
+        gids = torch.empty((Tg, K), dtype=torch.int32, device=self.dev)
+        gw = torch.empty((Tg, K), dtype=torch.float32, device=self.dev)
+        rdg.rdg_route(lg, cfg["n_group"], cfg["topk_group"], K, cfg["scale"], gids, gw)
+        self.l2p = torch.from_numpy(plan["log2phy"]).to(self.dev)
+        self.nrep = torch.from_numpy(plan["n_replica"]).to(self.dev)
+        gidx = torch.arange(Tg, dtype=torch.int64, device=self.dev)
+        loc = torch.empty_like(gids)
+        rdg.rdg_eplb_remap(gids, gidx, self.l2p, self.nrep, plan["phys_begin"], plan["n_local"], loc)
+        loc_np = loc.cpu().numpy()
+        toks, keep = synth.take_rank_rows(loc_np, cfg["rows"])
+        ids = gids.cpu().numpy()[toks]
+        ids[~keep & (loc_np[toks] >= 0)] = -1
+        sel = torch.from_numpy(toks).to(self.dev)
+        self.T = T = len(toks)
+        self.ids = torch.from_numpy(ids).to(self.dev)
+        self.tw = gw[sel].contiguous()
+        self.gidx = gidx[sel].contiguous()
+        self.local = torch.empty_like(self.ids)
+        self.x, self.x_s = self._quant(synth.x(cfg, T, device=self.dev))
+        phys2log = np.full(cfg["n_ranks"] * cfg["n_local"], -1)
+        for e in range(cfg["N"]):
+            for r in range(plan["n_replica"][e]):
+                phys2log[plan["log2phy"][e, r]] = e
+        self.W, self.S = self._experts([int(phys2log[plan["phys_begin"] + s]) for s in range(plan["n_local"])])
+        kind = rdg.RDG_MASKED if cfg["layout"] == "masked" else rdg.RDG_CONTIGUOUS
+        self._buffers(T, K, plan["n_local"], kind, block_m=128, m_max=cfg.get("m_max", 0))
+        self.out = torch.empty((T, cfg["H"]), dtype=self.ydt, device=self.dev)
+        self.signals = None
+        if cfg.get("signals"):
+            rows = rdg.rdg_signal_rows(self.L, self.DT, cfg["H"], cfg["I"])
+            self.signal_rows = rows
+            self.signals = torch.zeros(((self.L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=self.dev)
+            self.threshold = rdg.rdg_signal_threshold(cfg["H"], self.DT)
+            self.side = torch.cuda.Stream()
+        if cfg.get("shared_I"):
+            self.x_own, self.x_own_s = self._quant(synth.x(cfg, cfg["own_tokens"], device=self.dev, tensor=10))
+            self.Wsh, self.Ssh = self._experts([0], shared=True)
+            self._shared_buffers(cfg["own_tokens"])
+
+    # ------------------------------------------------------------ step
+    def _gate_up(self, timed):
+        rdg, cfg = self.rdg, self.cfg
+        if timed:
+            e0 = self.torch.cuda.Event(enable_timing=True)
+            e1 = self.torch.cuda.Event(enable_timing=True)
+            e0.record(self.stream)
+        rdg.rdg_grouped_gate_up(self.L, self.DT, cfg["H"], cfg["I"], self.x_perm, self.x_perm_s, self.W["W1"],
+                                self.W["W3"], self.S.get("W1"), self.S.get("W3"), self.h, self.h_s)
+        if timed:
+            e1.record(self.stream)
+            self.events.append((e0, e1))
+
+    def _shared(self, x, x_s, T, stream=None):
+        rdg, cfg = self.rdg, self.cfg
+        rdg.rdg_layout_dense(T, self.Ls, stream=stream)
+        rdg.rdg_grouped_ffn(self.Ls, self.DT, cfg["H"], cfg["shared_I"], x, x_s, self.Wsh["W1"], self.Wsh["W3"],
+                            self.Wsh["W2"], self.Ssh.get("W1"), self.Ssh.get("W3"), self.Ssh.get("W2"), self.hs,
+                            self.hs_s, self.ys, stream=stream)
+
+    def step(self, timed=False):
+        rdg, cfg = self.rdg, self.cfg
+        H, I, K = cfg["H"], cfg["I"], cfg["K"]
+        if not self.rank:
+            rdg.rdg_route(self.logits, cfg["n_group"], cfg["topk_group"], K, cfg["scale"], self.ids, self.tw)
+            rdg.rdg_dispatch(self.x, None, self.DT, self.ids, self.L, self.x_perm)
+            self._shared(self.x, None, self.T)
+            self._gate_up(timed)
+            rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
+            rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, self.ys, self.out, self.YDT)
+            return
+        plan = self.plan
+        rdg.rdg_eplb_remap(self.ids, self.gidx, self.l2p, self.nrep, plan["phys_begin"], plan["n_local"], self.local)
+        rdg.rdg_dispatch(self.x, self.x_s, self.DT, self.local, self.L, self.x_perm, self.x_perm_s)
+        if self.signals is None:
+            self._gate_up(timed)
+            rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
+            rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
+            return
+        # signalled down GEMM on this stream; shared expert + polling combine on the side stream
+        rdg.rdg_fill_i32(self.signals, 0)
+        self.side.wait_stream(self.stream)
+        self._gate_up(timed)
+        rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y,
+                             self.signals)
+        with self.torch.cuda.stream(self.side):
+            self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
+            rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
+                            self.signal_rows, self.threshold, 1_000_000, 64, stream=self.side)
+        self.stream.wait_stream(self.side)
 
 
 def main():
@@ -44,142 +246,100 @@ def main():
     import numpy as np
     import torch
 
-    import routing_dispatch_grouped_amd as rdg
-    import synth
-
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    cfg = synth.WORKLOADS[args.workload]
-    B, H, N, K, I, shI = cfg["B"], cfg["H"], cfg["N"], cfg["K"], cfg["I"], cfg["shared_I"]
-    m_max = cfg["m_max"]
-    DT = rdg.RDG_BF16
-
-    # ---------------------------------------------------------------- inputs (HBM-resident)
-    logits_np = synth.logits(cfg)
-    logits = torch.from_numpy(logits_np).to(dev)
-    x = synth.x(cfg, B, device=dev)
-    # weights are packed once into the grouped GEMMs' tile order (load time, not timed)
-    W1 = torch.empty((N, I, H), dtype=torch.bfloat16, device=dev)
-    W3 = torch.empty((N, I, H), dtype=torch.bfloat16, device=dev)
-    W2 = torch.empty((N, H, I), dtype=torch.bfloat16, device=dev)
-    for e in range(N):
-        w = synth.expert_weights(cfg, e, device=dev)
-        rdg.rdg_pack_weights(w["W1"], DT, W1[e]); rdg.rdg_pack_weights(w["W3"], DT, W3[e])
-        rdg.rdg_pack_weights(w["W2"], DT, W2[e])
-        del w
-    sh = synth.expert_weights(cfg, 0, device=dev, shared=True)
-    sW1, sW3, sW2 = (torch.empty_like(sh[k]).unsqueeze(0) for k in ("W1", "W3", "W2"))
-    for k, dst in (("W1", sW1), ("W3", sW3), ("W2", sW2)):
-        rdg.rdg_pack_weights(sh[k], DT, dst[0])
-
-    # ---------------------------------------------------------------- buffers
-    ids = torch.empty((B, K), dtype=torch.int32, device=dev)
-    tw = torch.empty((B, K), dtype=torch.float32, device=dev)
-    L = rdg.Layout(rdg.RDG_MASKED, N, B, K, dev, m_max=m_max)
-    x_perm = torch.empty((L.m_cap, H), dtype=torch.bfloat16, device=dev)
-    h = torch.empty((L.m_cap, I), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((L.m_cap, H), dtype=torch.bfloat16, device=dev)
-    Ls = rdg.Layout(rdg.RDG_CONTIGUOUS, 1, B, 1, dev, block_m=16, m_cap=B)
-    hs = torch.empty((B, shI), dtype=torch.bfloat16, device=dev)
-    ys = torch.empty((B, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((B, H), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-    ev = []
-
-    def step(timed=False):
-        rdg.rdg_route(logits, cfg["n_group"], cfg["topk_group"], K, cfg["scale"], ids, tw)
-        rdg.rdg_dispatch(x, None, DT, ids, L, x_perm)
-        rdg.rdg_layout_dense(B, Ls)
-        rdg.rdg_grouped_ffn(Ls, DT, H, shI, x, None, sW1, sW3, sW2, None, None, None, hs, None, ys)
-        if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-        rdg.rdg_grouped_gate_up(L, DT, H, I, x_perm, None, W1, W3, None, None, h, None)
-        if timed:
-            e1.record(stream)
-            ev.append((e0, e1))
-        rdg.rdg_grouped_down(L, DT, H, I, h, None, W2, None, y)
-        rdg.rdg_combine(y, DT, L, tw, B, K, H, ys, out, DT)
-
+    b = Bench(args.workload, dev)
+    rdg, cfg = b.rdg, b.cfg
     for _ in range(args.warmup):
-        step()
+        b.step()
     torch.cuda.synchronize()
-    code, detail = rdg.rdg_check_status(L)
+    code, detail = rdg.rdg_check_status(b.L)
     if code != 0:
         raise RuntimeError("device status %d (%s), detail %d" % (code, rdg.strerror(code), detail))
-    active = int((L.masked_m > 0).sum().item())
-    rows = int(L.masked_m.sum().item())
+    masked_m = b.L.masked_m.cpu().numpy()
+    active = int((masked_m > 0).sum())
+    rows = int(masked_m.sum())
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(timed=True)
+        b.step(timed=True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
-    gate_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    gate_ms = float(np.mean([a.elapsed_time(e) for a, e in b.events]))
 
-    # algorithmic bytes of one gate/up launch: W1 and W3 of every active expert,
-    # the routed rows of x_perm read once, h written once
-    gate_bytes = active * 2 * I * H * 2 + rows * H * 2 + rows * I * 2
-    achieved = gate_bytes / (gate_ms * 1e-3) / 1e9
-
-    line = {
-        "metric": "MoE-layer tokens/s on 1 MI355X",
-        "value": B / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": B, "H": H, "experts": N, "n_group": cfg["n_group"],
-                   "topk_group": cfg["topk_group"], "K": K, "I": I, "shared_I": shI, "layout": "masked",
-                   "m_max": m_max, "active_experts": active, "routed_rows": rows},
-        "roofline": {"kernel": "grouped gate/up GEMM (k_ffn, bf16, gated)", "bound": "hbm",
-                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": None, "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes},
-    }
-
-    if args.cpu_tokens > 0:
-        line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_tokens, logits_np, x, sh, dev)
+    H, I, K = cfg["H"], cfg["I"], cfg["K"]
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg["dtype"]]
+    # algorithmic work of one gate/up launch: W1 and W3 of every active expert
+    # (+ fp8 block scales), the routed rows of x_perm read once, h written once
+    gate_bytes = active * 2 * I * H * esz + rows * H * esz + rows * I * esz
+    if esz == 1:
+        gate_bytes += active * 2 * (I // 128) * (H // 128) * 4 + rows * (H // 128 + I // 128) * 4
+    gate_flops = 2 * 2 * rows * H * I
+    gbps = gate_bytes / (gate_ms * 1e-3) / 1e9
+    tflops = gate_flops / (gate_ms * 1e-3) / 1e12
+    peak_f = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+    hbm_frac, mfma_frac = gbps / HBM_PEAK_GBPS, tflops / peak_f
+    # the bound is the resource the roofline says limits this launch
+    hbm_bound = gate_bytes / (HBM_PEAK_GBPS * 1e9) >= gate_flops / (peak_f * 1e12)
+    roof = {"kernel": "grouped gate/up GEMM + SiLU-gated product (%s)" % cfg["dtype"],
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": gbps if hbm_bound else tflops, "peak": HBM_PEAK_GBPS if hbm_bound else peak_f,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": hbm_frac if hbm_bound else mfma_frac,
+            "traffic": None, "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes, "algorithmic_flops": gate_flops,
+            "hbm_frac": hbm_frac, "mfma_frac": mfma_frac}
+    if b.rank:
+        metric, unit = "MoE-layer token-equivalents/s (received rows / K) on 1 MI355X", "token-equivalents/s"
+        value = rows / K / (ms * 1e-3)
+    else:
+        metric, unit = "MoE-layer tokens/s on 1 MI355X", "tokens/s"
+        value = b.T / (ms * 1e-3)
+    conf = {"workload": args.workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
+            "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
+            "layout": cfg["layout"], "active_experts": active, "routed_rows": rows}
+    if "m_max" in cfg:
+        conf["m_max"] = cfg["m_max"]
+    if b.rank:
+        conf.update(local_experts=cfg["n_local"], ranks=cfg["n_ranks"], received_rows=rows)
+    line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof}
+    if args.cpu_tokens > 0 and not b.rank and args.workload == "decode_bf16":
+        line["cpu_baseline"] = cpu_baseline(b, args.cpu_tokens)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(cfg, n_tok, logits_np, x, sh, dev):
+def cpu_baseline(b, n_tok):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    routing of the whole batch and the layer output of the first n_tok tokens.
-    Host copies of the needed inputs are made before the clock starts."""
+    routing of the whole batch, the layout, and the layer output of the first
+    n_tok tokens.  Host copies of the needed inputs (from the generator) are
+    made before the clock starts."""
     import numpy as np
     import torch
 
     import oracle
+    cfg, synth = b.cfg, b.synth
 
     def u16(t):
         return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
-    ri, rw = oracle.route(logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+    ri, _ = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
     sel = np.arange(n_tok, dtype=np.int32)
     used = set(np.unique(ri[sel]).tolist())
-    import synth
-    experts = [{k: u16(v) for k, v in synth.expert_weights(cfg, e, device=dev).items()} if e in used else None
+    experts = [{k: u16(v) for k, v in synth.expert_weights(cfg, e, device=b.dev).items()} if e in used else None
                for e in range(cfg["N"])]
-    shared = {k: u16(v) for k, v in sh.items()}
-    xh = u16(x)
+    shared = {k: u16(v) for k, v in synth.expert_weights(cfg, 0, device=b.dev, shared=True).items()}
+    xh = u16(b.x)
     t0 = time.perf_counter()
-    ids, w = oracle.route(logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+    ids, w = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
     oracle.layout(ids, cfg["N"], oracle.MASKED, m_max=cfg["m_max"])
     oracle.moe_layer(oracle.BF16, xh, ids, w, experts, shared=shared, sel=sel)
     dt = time.perf_counter() - t0
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "seconds": dt,
             "sample": "route all %d tokens, layout, and the fp64 layer output (8 routed experts + shared) of "
-                      "the first %d tokens" % (logits_np.shape[0], n_tok)}
+                      "the first %d tokens" % (b.logits_np.shape[0], n_tok)}
 
 
 if __name__ == "__main__":

@@ -160,7 +160,7 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  * with 1x128 scales (h_scales_ws [m_cap, I/128]); y is bf16.
  *   h_ws      [m_cap, I] (dtype's storage: fp32 / bf16 / e4m3)
  *   y         [m_cap, H] fp32 (RDG_F32) or bf16
- *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype))] int32, zeroed by the
+ *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype, H, I))] int32, zeroed by the
  *             caller (rdg_fill_i32) before this call: after the down GEMM
  *             has stored a row tile's outputs for a block of columns it adds
  *             the block's column count to that tile's counter with release
@@ -198,9 +198,10 @@ int rdg_grouped_gate_up(const rdg_layout* L, int dtype, int H, int I, const void
 int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h_ws, const float* h_scales_ws,
                      const void* W2, const float* W2_s, void* y, int32_t* signals, rdg_stream_t stream);
 
-/* Rows per signal counter and the counter value that means "row tile done",
- * for the down GEMM of rdg_grouped_ffn on this layout. */
-int rdg_signal_rows(const rdg_layout* L, int dtype);
+/* Rows per signal counter (the grouped GEMMs' row tile for this layout,
+ * type and size: 16, 32, 64 or 128) and the counter value that means "row
+ * tile done" (H), for the down GEMM of rdg_grouped_ffn. */
+int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I);
 int rdg_signal_threshold(int H, int dtype);
 
 /* Combine ([DEEP] "EP": weighted sum back to the token; [DEEP] "why is
@@ -214,6 +215,7 @@ int rdg_signal_threshold(int H, int dtype);
  *   shared_out [T, H] in out_dtype, or NULL
  *   out        [T, H] out_dtype (RDG_F32 or RDG_BF16)
  *   signals    NULL, or the counters given to rdg_grouped_ffn, with
+ *              signal_rows = rdg_signal_rows(L, dtype, H, I) of that call,
  *              threshold and a timeout in microseconds (a tile still
  *              incomplete then is skipped and status = RDG_ETIMEOUT with
  *              detail = the tile index)
@@ -223,8 +225,8 @@ int rdg_signal_threshold(int H, int dtype);
  * The polling form may run on another stream concurrently with the down
  * GEMM, which must have been enqueued first. */
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
-                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int threshold,
-                int64_t timeout_us, int max_blocks, rdg_stream_t stream);
+                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
+                int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream);
 
 /* fp8 e4m3 block quantiser (the "1d2d" scales of [SBO] section 3): blocks of
  * block_rows x 128 (1 for activations, 128 for weights); scale = amax/448 in

@@ -47,9 +47,9 @@ _SIGS = {
     "rdg_grouped_ffn": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_grouped_gate_up": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_grouped_down": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
-    "rdg_signal_rows": ([_LP, _I], _I),
+    "rdg_signal_rows": ([_LP, _I, _I, _I], _I),
     "rdg_signal_threshold": ([_I, _I], _I),
-    "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I64, _I, _P], _I),
+    "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I64, _I, _P], _I),
     "rdg_quantize_fp8": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "rdg_fill_i32": ([_P, ctypes.c_int32, _I64, _P], _I),
     "rdg_packed_weight_bytes": ([_I, _I, _I, _I], _SZ),
@@ -168,8 +168,8 @@ def rdg_grouped_down(layout, dtype, H, I, h_ws, h_scales_ws, W2, W2_s, y, signal
                                  _ptr(y), _ptr(signals), _stream(stream)), "rdg_grouped_down")
 
 
-def rdg_signal_rows(layout, dtype):
-    r = _lib.rdg_signal_rows(layout.ref, dtype)
+def rdg_signal_rows(layout, dtype, H, I):
+    r = _lib.rdg_signal_rows(layout.ref, dtype, H, I)
     _check(min(r, 0), "rdg_signal_rows")
     return r
 
@@ -180,11 +180,11 @@ def rdg_signal_threshold(H, dtype):
     return r
 
 
-def rdg_combine(y, y_dtype, layout, topk_w, T, K, H, shared_out, out, out_dtype, signals=None, threshold=0,
-                timeout_us=0, max_blocks=0, stream=None):
+def rdg_combine(y, y_dtype, layout, topk_w, T, K, H, shared_out, out, out_dtype, signals=None, signal_rows=0,
+                threshold=0, timeout_us=0, max_blocks=0, stream=None):
     _check(_lib.rdg_combine(_ptr(y), y_dtype, layout.ref, _ptr(topk_w), T, K, H, _ptr(shared_out), _ptr(out),
-                            out_dtype, _ptr(signals), threshold, timeout_us, max_blocks, _stream(stream)),
-           "rdg_combine")
+                            out_dtype, _ptr(signals), signal_rows, threshold, timeout_us, max_blocks,
+                            _stream(stream)), "rdg_combine")
 
 
 def rdg_quantize_fp8(src, src_dtype, block_rows, q, scales, stream=None):

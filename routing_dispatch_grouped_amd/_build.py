@@ -11,7 +11,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librdg.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "quant.hip", "pack.hip", "ffn.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "quant.hip", "pack.hip", "ffn.hip", "ffn_tiled.hip", "combine.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

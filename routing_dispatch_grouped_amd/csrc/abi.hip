@@ -27,13 +27,19 @@ bool layout_ok(const rdg_layout* L) {
 }
 
 // The row tile of the grouped GEMMs for a layout: grows with the expected
-// rows per expert, and divides the segment alignment so that every tile
-// lies inside one expert and row / tile indexes a unique signal counter.
-int choose_bt(const rdg_layout* L) {
+// rows per expert (16: the skinny split-K kernels; 32/64: 128-column
+// register-tiled kernels; 128: the LDS-tiled kernels of ffn_tiled.hip, for
+// bf16/fp8 when both reduction dims split into 256-byte chunks), and divides
+// the segment alignment so that every tile lies inside one expert and
+// row / tile indexes a unique signal counter (a one-expert layout starts at
+// row 0, so any tile fits it).
+int choose_bt(const rdg_layout* L, int dtype, int H, int I) {
     const int64_t rows = L->n_rows;
     const int64_t avg = (rows + L->n_local - 1) / L->n_local;
     int want = avg <= 24 ? 16 : avg <= 48 ? 32 : 64;
-    const int align = L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
+    const int esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2 : 1;
+    if (dtype != RDG_F32 && avg > 48 && ((int64_t)H * esz) % 256 == 0 && ((int64_t)I * esz) % 256 == 0) want = 128;
+    const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
     while (want > 16 && align % want != 0) want /= 2;
     return want;
 }
@@ -118,10 +124,9 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream) {
     return hip_rc(launch_layout_dense(T, *L, stream));
 }
 
-int rdg_signal_rows(const rdg_layout* L, int dtype) {
-    (void)dtype;
-    if (!layout_ok(L)) return RDG_EINVAL;
-    return choose_bt(L);
+int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I) {
+    if (!layout_ok(L) || H < 128 || H % 128 != 0 || I < 128 || I % 128 != 0) return RDG_EINVAL;
+    return choose_bt(L, dtype, H, I);
 }
 
 int rdg_signal_threshold(int H, int dtype) {
@@ -145,9 +150,9 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     if (stages & 2) {
         if (!W2 || !y || !aligned16(W2) || !aligned16(y) || (fp8 && !W2_s)) return RDG_EINVAL;
     }
-    const int bt = choose_bt(L);
+    const int bt = choose_bt(L, dtype, H, I);
     if (signals) {
-        const int align = L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
+        const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
         if (align % bt != 0) return RDG_EUNSUPPORTED;
     }
     FfnCall c{};
@@ -198,8 +203,8 @@ int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h
 }
 
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
-                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int threshold,
-                int64_t timeout_us, int max_blocks, rdg_stream_t stream) {
+                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
+                int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream) {
     if (!layout_ok(L) || !L->pos || T < 0 || K < 1 || K > 32 || H < 8 || H % 8 != 0) return RDG_EINVAL;
     if ((int64_t)T * K != L->n_rows) return RDG_EINVAL;
     if (!((y_dtype == RDG_BF16 && (out_dtype == RDG_BF16 || out_dtype == RDG_F32)) ||
@@ -212,7 +217,8 @@ int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* to
     uint64_t ticks = 0;
     if (signals) {
         if (threshold < 1 || timeout_us < 0 || !L->status) return RDG_EINVAL;
-        rows_per_sig = choose_bt(L);
+        if (signal_rows != 16 && signal_rows != 32 && signal_rows != 64 && signal_rows != 128) return RDG_EINVAL;
+        rows_per_sig = signal_rows;
         ticks = (uint64_t)timeout_us * wall_ticks_per_us();
     }
     return hip_rc(launch_combine(y, y_dtype, L->pos, topk_w, T, K, H, shared_out, out, out_dtype, signals,

@@ -546,6 +546,7 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
 
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s) {
     if (c.n_tiles_max <= 0) return hipSuccess;
+    if (c.bt == 128) return launch_ffn_tiled(c, s);
     switch (c.dtype) {
         case RDG_F32: return launch_dt<RDG_F32>(c, s);
         case RDG_BF16: return launch_dt<RDG_BF16>(c, s);

@@ -134,6 +134,7 @@ struct FfnCall {
     int stages;  // bit 0: gate/up, bit 1: down
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s);  // bt == 128, bf16 / fp8
 
 hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
                           const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,

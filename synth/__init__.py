@@ -190,3 +190,25 @@ def eplb_plan(cfg):
     bottleneck = int(np.argmax(load))
     return dict(log2phy=log2phy, n_replica=n_rep, load=load, bottleneck=bottleneck,
                 phys_begin=bottleneck * n_local, n_local=n_local)
+
+
+def take_rank_rows(local_ids, rows):
+    """Which tokens one rank receives: given the global batch's per-slot
+    local expert ids on this rank (-1: not here), take the tokens that send
+    it at least one row, in global order, until exactly ``rows`` rows; the
+    last token's surplus rows are marked as not sent.  Returns (token
+    indices, keep mask [n_tokens, K])."""
+    local_ids = np.asarray(local_ids)
+    per_tok = (local_ids >= 0).sum(1)
+    toks, keep, taken = [], [], 0
+    for t in np.flatnonzero(per_tok > 0):
+        k_loc = np.flatnonzero(local_ids[t] >= 0)
+        m = np.zeros(local_ids.shape[1], bool)
+        take = k_loc[:rows - taken]
+        m[take] = True
+        toks.append(t)
+        keep.append(m)
+        taken += len(take)
+        if taken == rows:
+            break
+    return np.array(toks, dtype=np.int64), np.array(keep, dtype=bool).reshape(-1, local_ids.shape[1])

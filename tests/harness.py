@@ -129,8 +129,9 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
     y = torch.empty((L.m_cap, H), dtype=ydt, device=x.device)
     sig = None
     thr = 0
+    rows = 0
     if signals:
-        rows = m.rdg_signal_rows(L, dt)
+        rows = m.rdg_signal_rows(L, dt, H, I)
         sig = torch.empty(((L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=x.device)
         m.rdg_fill_i32(sig, 0)
         thr = m.rdg_signal_threshold(H, dt)
@@ -144,14 +145,16 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
         m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
                           experts.s3, experts.s2, h, h_s, y, sig, stream=s_gemm)
         with torch.cuda.stream(s_comb):
-            m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, thr, timeout_us,
-                          max_blocks, stream=s_comb)
+            m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0,
+                          thr, timeout_us, max_blocks, stream=s_comb)
         s_gemm.wait_stream(s_comb)
     else:
         m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
                           experts.s3, experts.s2, h, h_s, y, sig)
-        m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, thr, timeout_us, max_blocks)
-    return dict(L=L, x_perm=x_perm, x_perm_s=x_perm_s, h=h, h_s=h_s, y=y, out=out, signals=sig, threshold=thr)
+        m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0, thr,
+                      timeout_us, max_blocks)
+    return dict(L=L, x_perm=x_perm, x_perm_s=x_perm_s, h=h, h_s=h_s, y=y, out=out, signals=sig, threshold=thr,
+                signal_rows=rows)
 
 
 def run_shared(cfg, x, x_s, shared):

@@ -128,28 +128,16 @@ def rank_share(cfg):
                      torch.from_numpy(nrep).to(DEV), plan["phys_begin"], plan["n_local"], loc)
     rloc = oracle.eplb_remap(ri, gidx, l2p, nrep, plan["phys_begin"], plan["n_local"])
     assert np.array_equal(np_of(loc), rloc), "remap differs from the oracle"
-    per_tok = (rloc >= 0).sum(1)
-    toks, taken = [], 0
-    recv_ids = []
-    for t in np.flatnonzero(per_tok > 0):
-        row = ri[t].copy()
-        need = cfg["rows"] - taken
-        if per_tok[t] > need:
-            keep = np.flatnonzero(rloc[t] >= 0)[:need]
-            drop = [k for k in np.flatnonzero(rloc[t] >= 0) if k not in keep]
-            row[drop] = -1
-        toks.append(t)
-        recv_ids.append(row)
-        taken += min(per_tok[t], need)
-        if taken == cfg["rows"]:
-            break
-    toks = np.array(toks)
+    toks, keep = synth.take_rank_rows(rloc, cfg["rows"])
+    recv_ids = ri[toks].copy()
+    recv_ids[~keep & (rloc[toks] >= 0)] = -1   # surplus rows of the last token are not sent
+    taken = int(keep.sum())
     phys2log = np.full(cfg["n_ranks"] * cfg["n_local"], -1)
     for e in range(cfg["N"]):
         for r_ in range(nrep[e]):
             phys2log[l2p[e, r_]] = e
     local_logical = [int(phys2log[plan["phys_begin"] + s]) for s in range(plan["n_local"])]
-    return dict(plan=plan, tokens=toks, ids=np.stack(recv_ids).astype(np.int32), w=rw[toks], gidx=gidx[toks],
+    return dict(plan=plan, tokens=toks, ids=recv_ids.astype(np.int32), w=rw[toks], gidx=gidx[toks],
                 rows=taken, local_logical=local_logical, w_dev=w[torch.from_numpy(toks).to(DEV)].contiguous())
 
 
@@ -206,7 +194,7 @@ def test_prefill_rank_fp8_workload_sbo():
                                                                       signals=True, concurrent=True)
     # every row tile's counter reached the threshold exactly; unused counters stayed 0
     L = r["L"]
-    rows = m.rdg_signal_rows(L, m.RDG_FP8_E4M3)
+    rows = r["signal_rows"]
     sig = np_of(r["signals"])
     off = np_of(L.offsets)
     mm = np_of(L.masked_m)
@@ -274,7 +262,7 @@ def test_sbo_timeout_is_reported_not_hung():
     assert m.rdg_check_status(r["L"]) == (0, 0)
     out = torch.empty_like(r["out"])
     m.rdg_combine(r["y"], m.RDG_BF16, r["L"], w, B, cfg["K"], cfg["H"], None, out, m.RDG_BF16, r["signals"],
-                  r["threshold"] + 1, 2000, 4)
+                  r["signal_rows"], r["threshold"] + 1, 2000, 4)
     code, detail = m.rdg_check_status(r["L"])
     assert code == m.RDG_ETIMEOUT
     assert 0 <= detail < len(r["signals"])

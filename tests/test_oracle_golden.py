@@ -48,3 +48,13 @@ def test_eplb_and_rank_shares():
 def test_alignment_example():
     a = G["dense_ffn_alignment"]
     assert a["intermediate"] // a["tp"] == a["per_rank"] and a["per_rank"] % a["align"] != 0
+
+
+def test_take_rank_rows_exact_count():
+    import numpy as np
+    from synth import take_rank_rows
+    loc = np.array([[-1, -1], [0, -1], [-1, -1], [1, 2], [0, 3], [2, -1]])
+    toks, keep = take_rank_rows(loc, 3)
+    assert list(toks) == [1, 3] and keep.sum() == 3
+    toks, keep = take_rank_rows(loc, 4)
+    assert list(toks) == [1, 3, 4] and keep.sum() == 4 and list(keep[2]) == [True, False]
