@@ -40,7 +40,44 @@ def parse():
     p.add_argument("--workload", default="decode_bf16",
                    choices=["decode_bf16", "tiny_fp32", "prefill_bf16", "decode_rank_fp8", "prefill_rank_fp8"])
     p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
+                        "size, for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiling run)")
     return p.parse_args()
+
+
+# Files whose contents determine the dominant kernel's memory traffic; the
+# committed counter figures apply only while their hash is unchanged.
+TRAFFIC_SOURCES = ["routing_dispatch_grouped_amd/csrc/ffn.hip", "routing_dispatch_grouped_amd/csrc/rdg_internal.h",
+                   "routing_dispatch_grouped_amd/csrc/pack.hip", "routing_dispatch_grouped_amd/csrc/abi.hip"]
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in TRAFFIC_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary (profiles/traffic_<workload>.txt), or None when
+    it is missing or was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.txt" % workload)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != source_hash():
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class Bench:
@@ -287,7 +324,8 @@ def main():
             "bound": "hbm" if hbm_bound else "mfma",
             "achieved": gbps if hbm_bound else tflops, "peak": HBM_PEAK_GBPS if hbm_bound else peak_f,
             "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": hbm_frac if hbm_bound else mfma_frac,
-            "traffic": None, "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes, "algorithmic_flops": gate_flops,
+            "traffic": measured_traffic(args.workload), "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes,
+            "algorithmic_flops": gate_flops, "source_hash": source_hash(),
             "hbm_frac": hbm_frac, "mfma_frac": mfma_frac}
     if b.rank:
         metric, unit = "MoE-layer token-equivalents/s (received rows / K) on 1 MI355X", "token-equivalents/s"
@@ -307,6 +345,13 @@ def main():
             "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof}
     if args.cpu_tokens > 0 and not b.rank and args.workload == "decode_bf16":
         line["cpu_baseline"] = cpu_baseline(b, args.cpu_tokens)
+    if args.calibrate_copy:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(json.dumps(line), flush=True)
 
 
