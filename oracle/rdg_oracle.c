@@ -20,8 +20,8 @@
  *          "group-limited gating", "why is combine slower than dispatch",
  *          "limitations".
  * Where the pages leave a constant open (scoring function, group score,
- * renormalisation, fp8 scale rule) the oracle follows the workload
- * definitions that accompany the build and states the reading inline.
+ * renormalisation, fp8 scale rule) the oracle follows the definitions
+ * of the synthetic workloads and states the reading inline.
  *
  * Build: gcc -O2 -ffp-contract=off -fopenmp -shared -fPIC (no fast-math),
  * so that every float operation below is one IEEE-754 operation.
