@@ -26,22 +26,35 @@ bool layout_ok(const rdg_layout* L) {
     return L->counts && L->offsets && L->masked_m && L->work;
 }
 
-// The row tile of the grouped GEMMs for a layout: grows with the expected
-// rows per expert (16: the skinny split-K kernels; 32/64: 128-column
-// register-tiled kernels; 128: the LDS-tiled kernels of ffn_tiled.hip, for
-// bf16/fp8 when both reduction dims split into 256-byte chunks), and divides
-// the segment alignment so that every tile lies inside one expert and
-// row / tile indexes a unique signal counter (a one-expert layout starts at
-// row 0, so any tile fits it).
-int choose_bt(const rdg_layout* L, int dtype, int H, int I) {
+// The row tile of the grouped GEMMs for a layout and the kernel family that
+// runs it.  The tile grows with the expected rows per expert: 16 (skinny
+// split-K kernels, weights streamed once per tile), 32/64 (128-column
+// register-tiled kernels), 128 (the LDS-tiled kernels of ffn_tiled.hip, for
+// bf16/fp8 when both reduction dims split into 256-byte chunks).  A dense
+// one-expert layout of at most 256 rows (a decode batch through the shared
+// expert) is weight-streaming work that a 128-row tile would spread over too
+// few workgroups: it takes the skinny kernels with up to four 16-row tiles
+// per workgroup.  The tile divides the segment alignment, so that every tile
+// lies inside one expert and row / tile indexes a unique signal counter (a
+// one-expert layout starts at row 0, so any tile fits it).
+struct FfnPlan {
+    int bt;  // rows per tile
+    int nr;  // > 0: skinny kernels with nr 16-row tiles per workgroup
+};
+
+FfnPlan plan_ffn(const rdg_layout* L, int dtype, int H, int I) {
     const int64_t rows = L->n_rows;
+    if (L->n_local == 1 && rows <= 256) {
+        const int nr = rows <= 16 ? 1 : rows <= 32 ? 2 : 4;
+        return FfnPlan{16 * nr, nr};
+    }
     const int64_t avg = (rows + L->n_local - 1) / L->n_local;
     int want = avg <= 24 ? 16 : avg <= 48 ? 32 : 64;
     const int esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2 : 1;
     if (dtype != RDG_F32 && avg > 48 && ((int64_t)H * esz) % 256 == 0 && ((int64_t)I * esz) % 256 == 0) want = 128;
     const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
     while (want > 16 && align % want != 0) want /= 2;
-    return want;
+    return FfnPlan{want, want == 16 ? 1 : 0};
 }
 
 int64_t ffn_tiles_max(const rdg_layout* L, int bt) {
@@ -126,7 +139,7 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream) {
 
 int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I) {
     if (!layout_ok(L) || H < 128 || H % 128 != 0 || I < 128 || I % 128 != 0) return RDG_EINVAL;
-    return choose_bt(L, dtype, H, I);
+    return plan_ffn(L, dtype, H, I).bt;
 }
 
 int rdg_signal_threshold(int H, int dtype) {
@@ -150,7 +163,8 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     if (stages & 2) {
         if (!W2 || !y || !aligned16(W2) || !aligned16(y) || (fp8 && !W2_s)) return RDG_EINVAL;
     }
-    const int bt = choose_bt(L, dtype, H, I);
+    const FfnPlan plan = plan_ffn(L, dtype, H, I);
+    const int bt = plan.bt;
     if (signals) {
         const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
         if (align % bt != 0) return RDG_EUNSUPPORTED;
@@ -162,6 +176,7 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     c.n_local = L->n_local;
     c.n_tiles_max = (int)ffn_tiles_max(L, bt);
     c.bt = bt;
+    c.skinny_nr = plan.nr;
     c.dtype = dtype;
     c.H = H;
     c.I = I;

@@ -46,6 +46,9 @@ struct Mma<RDG_F32> {
     __device__ static op_t load_tile(const uint8_t* tile, int lane) {
         return __builtin_nontemporal_load(reinterpret_cast<const float*>(tile) + lane);
     }
+    __device__ static op_t load_tile_cached(const uint8_t* tile, int lane) {
+        return reinterpret_cast<const float*>(tile)[lane];
+    }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
         return reinterpret_cast<const float*>(row)[k0 + (lane >> 4)];
     }
@@ -61,6 +64,9 @@ struct Mma<RDG_BF16> {
     static constexpr int KS = 32, ESZ = 2, U = 4, BLK = 1024;
     __device__ static op_t load_tile(const uint8_t* tile, int lane) {
         return __builtin_nontemporal_load(reinterpret_cast<const bf16x8_t*>(tile + lane * 16));
+    }
+    __device__ static op_t load_tile_cached(const uint8_t* tile, int lane) {
+        return *reinterpret_cast<const bf16x8_t*>(tile + lane * 16);
     }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
         return *reinterpret_cast<const bf16x8_t*>(row + (size_t)(k0 + (lane >> 4) * 8) * 2);
@@ -82,6 +88,14 @@ struct Mma<RDG_FP8_E4M3> {
         op_t r;
         r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
         r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+        return r;
+    }
+    __device__ static op_t load_tile_cached(const uint8_t* tile, int lane) {
+        const uint4 a = *reinterpret_cast<const uint4*>(tile + lane * 16);
+        const uint4 b = *reinterpret_cast<const uint4*>(tile + 1024 + lane * 16);
+        op_t r;
+        r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+        r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
         return r;
     }
     __device__ static op_t load(const uint8_t* row, int k0, int lane) {
@@ -314,25 +328,32 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
 
 
 // ---------------------------------------------------------------------------
-// Skinny variant for row tiles of at most 16 rows (decode: a few tokens per
-// expert).  Each workgroup owns 16*FPW weight rows of one expert; its four
-// waves split the reduction dimension in four contiguous ranges of 128-wide
-// blocks, and the partial sums are added in LDS in wave order (so the result
-// does not depend on timing).  Many short workgroups instead of few long
-// ones keep the last round of the grid from idling most of the GPU.  Used for
-// every type except the fp8 gate/up stage, whose 1x128 re-quantisation of h
-// needs 128 columns in one workgroup.
-template <int DT, bool GATED, bool SIGNAL, int FPW>
+// Skinny variant for weight-streaming row tiles (decode: a few tokens per
+// expert; a dense expert of up to a few hundred tokens).  Each workgroup owns
+// 16*FPW weight rows of one expert and NR consecutive 16-row tiles of its
+// tokens (BT = 16*NR rows); its four waves split the reduction dimension in
+// four contiguous ranges of 128-wide blocks, and the partial sums are added
+// in LDS in wave order (so the result does not depend on timing).  Many short
+// workgroups instead of few long ones keep the last round of the grid from
+// idling most of the GPU.  With NR = 1 an expert's weights are read once per
+// 16-row tile and are streamed past the caches; with NR > 1 the row groups of
+// one weight panel re-read it, so the loads stay cacheable.  Used for every
+// type except the fp8 gate/up stage, whose 1x128 re-quantisation of h needs
+// 128 columns in one workgroup.
+template <int DT, bool GATED, bool SIGNAL, int FPW, int NR>
 __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     using M = Mma<DT>;
     using op_t = typename M::op_t;
-    constexpr int KS = M::KS, U = M::U, ESZ = M::ESZ;
+    constexpr int KS = M::KS, ESZ = M::ESZ;
+    // fewer K steps in flight as the token operand grows (register budget)
+    constexpr int U = DT == RDG_FP8_E4M3 ? 1 : NR <= 2 ? M::U : M::U / 2 > 0 ? M::U / 2 : 1;
     constexpr int G = GATED ? 2 : 1;
+    constexpr int BT = 16 * NR;
     constexpr int OUT_KIND = DT == RDG_F32 ? 0 : 1;
     // each wave walks whole 128-element blocks of the reduction dimension in
     // steps of KS*U, so a step must never run past the end of its block
     static_assert(DT == RDG_FP8_E4M3 || 128 % (KS * U) == 0, "KS * U must divide 128");
-    __shared__ f32x4_t part[4][FPW * G][kWave];
+    __shared__ f32x4_t part[4][FPW * G * NR][kWave];
 
     const int tile = blockIdx.x;
     const int n_tiles = a.tile_off[a.n_local];
@@ -344,7 +365,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         else hi = mid;
     }
     const int e = lo;
-    const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * 16;
+    const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
     const int f0 = blockIdx.y * (16 * FPW);
     const int wv = threadIdx.x / kWave, lane = lane_id();
@@ -359,16 +380,25 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         arow[rt] = a.Wa + grp * nks * M::BLK;
         brow[rt] = GATED ? a.Wb + grp * nks * M::BLK : nullptr;
     }
-    const int xr = row0 + (lane & 15);
-    const bool xv = xr < row_end;
-    const uint8_t* xrow = a.X + (size_t)(xv ? xr : row0) * wstride;
-
-    f32x4_t accA[FPW], accB[FPW];
+    int xr[NR];
+    bool xv[NR];
+    const uint8_t* xrow[NR];
 #pragma unroll
-    for (int rt = 0; rt < FPW; ++rt) {
-        accA[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        accB[rt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int nr = 0; nr < NR; ++nr) {
+        xr[nr] = row0 + nr * 16 + (lane & 15);
+        xv[nr] = xr[nr] < row_end;
+        xrow[nr] = a.X + (size_t)(xv[nr] ? xr[nr] : row0) * wstride;
     }
+    auto wload = [&](const uint8_t* t) { return NR == 1 ? M::load_tile(t, lane) : M::load_tile_cached(t, lane); };
+
+    f32x4_t accA[FPW][NR], accB[FPW][NR];
+#pragma unroll
+    for (int rt = 0; rt < FPW; ++rt)
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr) {
+            accA[rt][nr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            accB[rt][nr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        }
     const int nkb = a.Kdim / 128;
     const int kb0 = (wv * nkb) / 4, kb1 = ((wv + 1) * nkb) / 4;
     const float* was = nullptr;
@@ -381,67 +411,79 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         if (DT != RDG_FP8_E4M3) {
 #pragma unroll
             for (int k0 = kb * 128; k0 < kb * 128 + 128; k0 += KS * U) {
-                op_t ra[U][FPW], rb[U][FPW], rx[U];
+                op_t ra[U][FPW], rb[U][FPW], rx[U][NR];
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
 #pragma unroll
                     for (int rt = 0; rt < FPW; ++rt) {
                         const size_t t_off = (size_t)(k0 / KS + u) * M::BLK;
-                        ra[u][rt] = M::load_tile(arow[rt] + t_off, lane);
-                        if (GATED) rb[u][rt] = M::load_tile(brow[rt] + t_off, lane);
+                        ra[u][rt] = wload(arow[rt] + t_off);
+                        if (GATED) rb[u][rt] = wload(brow[rt] + t_off);
                     }
-                    rx[u] = xv ? M::load(xrow, k0 + u * KS, lane) : M::zero();
+#pragma unroll
+                    for (int nr = 0; nr < NR; ++nr) rx[u][nr] = xv[nr] ? M::load(xrow[nr], k0 + u * KS, lane) : M::zero();
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u)
 #pragma unroll
-                    for (int rt = 0; rt < FPW; ++rt) {
-                        accA[rt] = M::mma(accA[rt], ra[u][rt], rx[u]);
-                        if (GATED) accB[rt] = M::mma(accB[rt], rb[u][rt], rx[u]);
-                    }
+                    for (int rt = 0; rt < FPW; ++rt)
+#pragma unroll
+                        for (int nr = 0; nr < NR; ++nr) {
+                            accA[rt][nr] = M::mma(accA[rt][nr], ra[u][rt], rx[u][nr]);
+                            if (GATED) accB[rt][nr] = M::mma(accB[rt][nr], rb[u][rt], rx[u][nr]);
+                        }
             }
         } else {
             op_t ra[FPW], rb[FPW];
 #pragma unroll
             for (int rt = 0; rt < FPW; ++rt) {
-                ra[rt] = M::load_tile(arow[rt] + (size_t)kb * M::BLK, lane);
-                if (GATED) rb[rt] = M::load_tile(brow[rt] + (size_t)kb * M::BLK, lane);
+                ra[rt] = wload(arow[rt] + (size_t)kb * M::BLK);
+                if (GATED) rb[rt] = wload(brow[rt] + (size_t)kb * M::BLK);
             }
-            const op_t rx = xv ? M::load(xrow, kb * 128, lane) : M::zero();
-            const float sx = xv ? a.Xs[(size_t)xr * nkb + kb] : 0.0f;
-            const float fa = sx * was[kb], fb = GATED ? sx * wbs[kb] : 0.0f;
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int rt = 0; rt < FPW; ++rt) {
-                accA[rt] += M::mma(z, ra[rt], rx) * fa;
-                if (GATED) accB[rt] += M::mma(z, rb[rt], rx) * fb;
+            for (int nr = 0; nr < NR; ++nr) {
+                const op_t rx = xv[nr] ? M::load(xrow[nr], kb * 128, lane) : M::zero();
+                const float sx = xv[nr] ? a.Xs[(size_t)xr[nr] * nkb + kb] : 0.0f;
+                const float fa = sx * was[kb], fb = GATED ? sx * wbs[kb] : 0.0f;
+#pragma unroll
+                for (int rt = 0; rt < FPW; ++rt) {
+                    accA[rt][nr] += M::mma(z, ra[rt], rx) * fa;
+                    if (GATED) accB[rt][nr] += M::mma(z, rb[rt], rx) * fb;
+                }
             }
         }
     }
     // reduce the four K ranges in wave order
 #pragma unroll
-    for (int rt = 0; rt < FPW; ++rt) {
-        part[wv][rt * G][lane] = accA[rt];
-        if (GATED) part[wv][rt * G + 1][lane] = accB[rt];
-    }
+    for (int rt = 0; rt < FPW; ++rt)
+#pragma unroll
+        for (int nr = 0; nr < NR; ++nr) {
+            part[wv][(rt * NR + nr) * G][lane] = accA[rt][nr];
+            if (GATED) part[wv][(rt * NR + nr) * G + 1][lane] = accB[rt][nr];
+        }
     __syncthreads();
-    if (wv == 0) {
-        const int row = row0 + (lane & 15);
-        const int fl = f0 + (lane >> 4) * 4;
+    // wave w finishes row tiles nr = w, w+4, ... (every wave when NR >= 4)
+    const int fl = (lane >> 4) * 4;
+#pragma unroll
+    for (int nr = 0; nr < NR; ++nr) {
+        if (nr % 4 != wv) continue;
+        const int row = row0 + nr * 16 + (lane & 15);
 #pragma unroll
         for (int rt = 0; rt < FPW; ++rt) {
-            f32x4_t g = part[0][rt * G][lane];
-            f32x4_t u = GATED ? part[0][rt * G + 1][lane] : g;
+            const int slot = (rt * NR + nr) * G;
+            f32x4_t g = part[0][slot][lane];
+            f32x4_t u = GATED ? part[0][slot + 1][lane] : g;
 #pragma unroll
             for (int w = 1; w < 4; ++w) {
-                g += part[w][rt * G][lane];
-                if (GATED) u += part[w][rt * G + 1][lane];
+                g += part[w][slot][lane];
+                if (GATED) u += part[w][slot + 1][lane];
             }
             float v[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) v[r] = GATED ? g[r] / (1.0f + __expf(-g[r])) * u[r] : g[r];
             if (row < row_end) {
-                const size_t idx = (size_t)row * a.Nout + fl + rt * 16;
+                const size_t idx = (size_t)row * a.Nout + f0 + fl + rt * 16;
                 if (OUT_KIND == 0) {
                     *reinterpret_cast<float4*>(a.O + idx * 4) = make_float4(v[0], v[1], v[2], v[3]);
                 } else {
@@ -457,22 +499,18 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         __threadfence();
         __syncthreads();
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / 16, 16 * FPW, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(a.signals + row0 / BT, 16 * FPW, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 
-template <int DT, int BT>
-hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
-    constexpr int ESZ = Mma<DT>::ESZ;
-    const int hsz = DT == RDG_F32 ? 4 : DT == RDG_BF16 ? 2 : 1;
+KArgs gate_up_args(const FfnCall& c) {
     KArgs g{};
     g.offsets = c.offsets;
     g.masked_m = c.masked_m;
     g.tile_off = c.tile_off;
     g.n_local = c.n_local;
-    // gate/up: Kdim = H, Nout = I
-    g.Kdim = c.H;
+    g.Kdim = c.H;  // gate/up: Kdim = H, Nout = I
     g.Nout = c.I;
     g.X = static_cast<const uint8_t*>(c.x);
     g.Xs = c.x_s;
@@ -483,28 +521,16 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     g.O = static_cast<uint8_t*>(c.h);
     g.Os = c.h_s;
     g.signals = nullptr;
-    (void)ESZ;
-    dim3 block(256);
-    constexpr bool kSkinny = BT == 16;
-    if (c.stages & 1) {
-        if (kSkinny && DT != RDG_FP8_E4M3) {
-            dim3 grid1(c.n_tiles_max, c.I / 32);
-            k_ffn_skinny<DT, true, false, 2><<<grid1, block, 0, s>>>(g);
-        } else {
-            dim3 grid1(c.n_tiles_max, c.I / 128);
-            k_ffn<DT, BT, true, false><<<grid1, block, 0, s>>>(g);
-        }
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
-    if (!(c.stages & 2)) return hipSuccess;
-    // down: Kdim = I, Nout = H, input h
+    return g;
+}
+
+KArgs down_args(const FfnCall& c) {
     KArgs d{};
     d.offsets = c.offsets;
     d.masked_m = c.masked_m;
     d.tile_off = c.tile_off;
     d.n_local = c.n_local;
-    d.Kdim = c.I;
+    d.Kdim = c.I;  // down: Kdim = I, Nout = H, input h
     d.Nout = c.H;
     d.X = static_cast<const uint8_t*>(c.h);
     d.Xs = c.h_s;
@@ -515,15 +541,52 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     d.O = static_cast<uint8_t*>(c.y);
     d.Os = nullptr;
     d.signals = c.signals;
-    (void)hsz;
-    if (kSkinny) {
-        dim3 grid2(c.n_tiles_max, c.H / 32);
+    return d;
+}
+
+// Row tiles of BT = 16*NR rows through the skinny kernel (the fp8 gate/up
+// stage through k_ffn, see above).  Gate/up: 32 weight rows per matrix and
+// workgroup for single 16-row tiles, 16 for NR > 1 (twice the workgroups, so
+// that a dense expert of a few row groups still fills the GPU); down: 32.
+template <int DT, int NR>
+hipError_t launch_skinny(const FfnCall& c, hipStream_t s) {
+    constexpr int BT = 16 * NR;
+    dim3 block(256);
+    if (c.stages & 1) {
+        const KArgs g = gate_up_args(c);
+        if constexpr (DT == RDG_FP8_E4M3) {
+            k_ffn<DT, BT, true, false><<<dim3(c.n_tiles_max, c.I / 128), block, 0, s>>>(g);
+        } else if constexpr (NR == 1) {
+            k_ffn_skinny<DT, true, false, 2, NR><<<dim3(c.n_tiles_max, c.I / 32), block, 0, s>>>(g);
+        } else {
+            k_ffn_skinny<DT, true, false, 1, NR><<<dim3(c.n_tiles_max, c.I / 16), block, 0, s>>>(g);
+        }
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (c.stages & 2) {
+        const KArgs d = down_args(c);
+        const dim3 grid2(c.n_tiles_max, c.H / 32);
         if (c.signals)
-            k_ffn_skinny<DT, false, true, 2><<<grid2, block, 0, s>>>(d);
+            k_ffn_skinny<DT, false, true, 2, NR><<<grid2, block, 0, s>>>(d);
         else
-            k_ffn_skinny<DT, false, false, 2><<<grid2, block, 0, s>>>(d);
-    } else {
-        dim3 grid2(c.n_tiles_max, c.H / 128);
+            k_ffn_skinny<DT, false, false, 2, NR><<<grid2, block, 0, s>>>(d);
+    }
+    return hipGetLastError();
+}
+
+// Row tiles of 32 or 64 rows through k_ffn (register-resident token tiles).
+template <int DT, int BT>
+hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
+    dim3 block(256);
+    if (c.stages & 1) {
+        k_ffn<DT, BT, true, false><<<dim3(c.n_tiles_max, c.I / 128), block, 0, s>>>(gate_up_args(c));
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    if (c.stages & 2) {
+        const KArgs d = down_args(c);
+        const dim3 grid2(c.n_tiles_max, c.H / 128);
         if (c.signals)
             k_ffn<DT, BT, false, true><<<grid2, block, 0, s>>>(d);
         else
@@ -534,8 +597,16 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
 
 template <int DT>
 hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
+    if (c.skinny_nr > 0) {
+        if (c.bt != 16 * c.skinny_nr) return hipErrorInvalidValue;
+        switch (c.skinny_nr) {
+            case 1: return launch_skinny<DT, 1>(c, s);
+            case 2: return launch_skinny<DT, 2>(c, s);
+            case 4: return launch_skinny<DT, 4>(c, s);
+            default: return hipErrorInvalidValue;
+        }
+    }
     switch (c.bt) {
-        case 16: return launch_bt<DT, 16>(c, s);
         case 32: return launch_bt<DT, 32>(c, s);
         case 64: return launch_bt<DT, 64>(c, s);
         default: return hipErrorInvalidValue;

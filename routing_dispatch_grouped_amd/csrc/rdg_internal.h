@@ -124,6 +124,7 @@ struct FfnCall {
     const int32_t* masked_m;
     const int32_t* tile_off;  // prefix table for row tile bt
     int n_local, n_tiles_max, bt;
+    int skinny_nr;  // > 0: skinny kernel with bt = 16 * skinny_nr (weight streaming)
     int dtype, H, I;
     const void *x, *W1, *W3, *W2;
     const float *x_s, *W1_s, *W3_s, *W2_s;

@@ -95,6 +95,31 @@ def test_small_layers(dtype, B, N, kind):
     _full_layer(cfg, B, kind, block_m=128, m_max=m_max)
 
 
+# a dense expert of T rows (the shared expert): T <= 256 takes the skinny
+# kernels with 1, 2 or 4 16-row tiles per workgroup (several row groups and a
+# ragged tail at T = 100 and 256 - 3); larger T the 128-row tiled kernels
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("T", [1, 16, 29, 64, 100, 253, 300])
+def test_dense_expert(dtype, T):
+    m = rdg()
+    cfg = _small_cfg(dtype, H=1024, I=512, wid=400 + T)
+    x = synth.x(cfg, T, device=DEV)
+    x_s, xo, xo_s = None, np_of(x), None
+    if dtype == "fp8":
+        x, x_s = quantize_act(x)
+        xo, xo_s = oracle.quantize_fp8(xo, 1)
+        assert np.array_equal(np_of(x), xo) and np.array_equal(np_of(x_s), xo_s)
+    shared = ExpertSet(cfg, [0], shared=True)
+    got = np_of(run_shared(cfg, x, x_s, shared))
+    ids = np.full((T, 1), -1, dtype=np.int32)
+    ref = oracle.moe_layer(dt_code(cfg), xo, ids, np.zeros((T, 1), np.float32), [None],
+                           shared=shared.oracle_expert(0), x_scales=xo_s)
+    err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
+    check_rows(got, ref, cfg, "dense %s T=%d" % (dtype, T))
+    print("dense expert %s T=%d rel_err=%.3e" % (dtype, T, err), flush=True)
+    assert err <= tolerance(cfg), err
+
+
 def test_tiny_fp32_workload():
     cfg = dict(synth.WORKLOADS["tiny_fp32"], name="tiny_fp32")
     _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=16)
