@@ -30,7 +30,7 @@ bool layout_ok(const rdg_layout* L) {
 // runs it.  The tile grows with the expected rows per expert: 16 (skinny
 // split-K kernels, weights streamed once per tile), 32/64 (128-column
 // register-tiled kernels), 128 (the LDS-tiled kernels of ffn_tiled.hip, for
-// bf16/fp8 when both reduction dims split into 256-byte chunks).  A dense
+// bf16/fp8 in the shapes tiled_supported accepts).  A dense
 // one-expert layout of at most 256 rows (a decode batch through the shared
 // expert) is weight-streaming work that a 128-row tile would spread over too
 // few workgroups: it takes the skinny kernels with up to four 16-row tiles
@@ -50,8 +50,7 @@ FfnPlan plan_ffn(const rdg_layout* L, int dtype, int H, int I) {
     }
     const int64_t avg = (rows + L->n_local - 1) / L->n_local;
     int want = avg <= 24 ? 16 : avg <= 48 ? 32 : 64;
-    const int esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2 : 1;
-    if (dtype != RDG_F32 && avg > 48 && ((int64_t)H * esz) % 256 == 0 && ((int64_t)I * esz) % 256 == 0) want = 128;
+    if (avg > 48 && tiled_supported(dtype, H, I)) want = 128;
     const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
     while (want > 16 && align % want != 0) want /= 2;
     return FfnPlan{want, want == 16 ? 1 : 0};

@@ -1,39 +1,58 @@
 // Grouped expert FFN for row tiles of 128 rows (prefill, rank shares, the
-// shared expert): the same two stages as ffn.hip -- gate/up GEMM with the
-// SiLU-gated product (and fp8 re-quantisation of h) in its epilogue, then the
-// down GEMM, optionally signalling each finished row tile -- with the
-// operand reuse a 128 x 128 output tile needs to approach the MFMA rate.
+// shared expert of a prefill batch): the same two stages as ffn.hip -- gate/up
+// GEMM with the SiLU-gated product (and fp8 re-quantisation of h) in its
+// epilogue, then the down GEMM, optionally signalling each finished row tile
+// -- with the operand reuse and the load pipeline a 128-row tile needs to
+// approach the MFMA rate.
 //
 // What it computes: see ffn.hip (DeepEP deep-dive, EP section; H100
 // deployment article, "DeepGEMM integration"; DeepGEMM single-batch-overlap
 // pull request, sections 2-3).
 //
-// Design for CDNA4.  A workgroup (8 waves, two per SIMD) owns 128 output
-// columns of one expert (128 rows of W1 and of W3 when gated) and a tile of
-// 128 layout rows.  Gated, wave w accumulates W1 (w < 4) or W3 for columns
-// [32(w%4), +32) over all 128 rows, and the W3 waves hand their sums to the
-// W1 waves through LDS for the SiLU-gated product; otherwise wave w covers
-// columns [32(w%4), +32) for rows [64(w/4), +64).  Weight operand tiles are
-// private to a wave and are loaded straight from the packed weights into
-// registers ahead of use (bf16: a chunk ahead; fp8: a step ahead).  The 128-row token tile is
-// shared by the eight waves, so it goes through LDS: each chunk (256 bytes of every row) is
-// fetched with direct global->LDS loads into a double buffer, and the slot of
-// 16-byte piece c of row r is c ^ (r % 16) (chosen through each lane's source
-// address), which makes the MFMA-layout LDS reads conflict-free.  Workgroups
-// are renumbered so that the token tiles sharing one weight panel run back to
-// back on the same XCD and re-read the panel from that XCD's L2.
+// Design for CDNA4.  A workgroup is 8 waves (two per SIMD) and owns a tile of
+// 128 layout rows of one expert and a panel of 256 weight rows: gated, rows
+// [f0, f0+128) of W1 (waves 0-3) and of W3 (waves 4-7); down, rows [f0,
+// f0+256) of W2.  Wave w owns 32 weight rows (two 16-row MFMA tiles) against
+// all 128 token rows (eight 16-row MFMA tiles), so each token operand read
+// from LDS feeds two MFMAs and each weight operand eight.
+//
+// The reduction dimension is walked in chunks of 256 bytes per row.  The
+// token tile is shared by the eight waves, so its chunks go through a
+// two-slot LDS ring filled by direct global->LDS loads; the slot of 16-byte
+// piece c of row r is c ^ (r % 16) (chosen through each lane's source
+// address), which makes the MFMA-layout LDS reads conflict-free.  Weight
+// operand tiles are private to a wave and arrive packed (pack.hip: one
+// contiguous KiB per load instruction) straight into one of two register
+// sets; a weight panel is re-read by every row tile of its expert, mostly
+// from L2.  While chunk k is multiplied, chunk k+1's token rows (into the
+// other ring slot) and weights (into the other register set) are in flight;
+// the loop is unrolled by two so that slots and register sets are named at
+// compile time (no register copies that would wait for a load in flight, and
+// the compiler can tell the slots apart), with one wait and one barrier per
+// chunk.
+// fp8 tiles also stage each chunk's activation scales (two 1x128 blocks per
+// row) through the ring; every 128-long block's MFMA partial is promoted into
+// the fp32 accumulator with its activation and weight scales.
+//
+// Workgroups are renumbered so that the token tiles sharing one weight panel
+// run back to back on the same XCD and re-read the panel from its L2.
 #include "rdg_internal.h"
 
 namespace rdg {
 namespace {
 
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-typedef int i32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int TB = 128;          // rows per tile
-constexpr int CB = 256;          // bytes of each row per staged chunk
-constexpr int CHUNK_LDS = TB * CB;
+constexpr int NW = 8;                 // waves per workgroup
+constexpr int TB = 128;               // rows per tile
+constexpr int CB = 256;               // bytes of each row per chunk
+constexpr int CHUNK_LDS = TB * CB;    // token bytes per chunk
+constexpr int XLOADS = CHUNK_LDS / 1024 / NW;  // KiB loads per wave and chunk
+constexpr int NCT = TB / 16;          // 16-row token tiles per wave
+constexpr int NRT = 2;                // 16-row weight tiles per wave
+constexpr int PANEL = NW * NRT * 16;  // weight rows per workgroup
 
 template <int DT>
 struct TOp;
@@ -41,9 +60,14 @@ struct TOp;
 template <>
 struct TOp<RDG_BF16> {
     using op_t = bf16x8_t;
-    static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);  // 4 steps per chunk
-    __device__ static op_t load_w(const uint8_t* tile, int lane) {
-        return *reinterpret_cast<const bf16x8_t*>(tile + lane * 16);
+    static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);  // 4 MFMA steps per chunk
+    static constexpr int WLOADS = NRT * STEPS;                                   // load instructions
+    __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                w[s][rt] = *reinterpret_cast<const bf16x8_t*>(wt[rt] + (size_t)(t0 + s) * BLK + lane * 16);
     }
     // token operand of step s for local row r, lane group g: 16-byte piece 4s+g
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
@@ -58,14 +82,21 @@ struct TOp<RDG_BF16> {
 template <>
 struct TOp<RDG_FP8_E4M3> {
     using op_t = i32x8_t;
-    static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // 2 steps per chunk
-    __device__ static op_t load_w(const uint8_t* tile, int lane) {
-        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(tile + lane * 16);
-        const i32x4_t b = *reinterpret_cast<const i32x4_t*>(tile + 1024 + lane * 16);
-        op_t r;
-        r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
-        r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
-        return r;
+    static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // 2 MFMA steps (scale blocks) per chunk
+    static constexpr int WLOADS = NRT * STEPS * 2;
+    __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) {
+                const uint8_t* tile = wt[rt] + (size_t)(t0 + s) * BLK;
+                const i32x4_t a = *reinterpret_cast<const i32x4_t*>(tile + lane * 16);
+                const i32x4_t b = *reinterpret_cast<const i32x4_t*>(tile + 1024 + lane * 16);
+                op_t r;
+                r[0] = a[0]; r[1] = a[1]; r[2] = a[2]; r[3] = a[3];
+                r[4] = b[0]; r[5] = b[1]; r[6] = b[2]; r[7] = b[3];
+                w[s][rt] = r;
+            }
     }
     // 32 bytes: pieces 8s+2g and 8s+2g+1
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
@@ -98,35 +129,69 @@ struct TArgs {
     int32_t* signals;
 };
 
-constexpr int NW = 8;            // waves per workgroup
+// s_waitcnt immediate (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8) that waits until at most N vector-memory instructions
+// are outstanding and leaves the other counters alone.
+template <int N>
+constexpr int vmcnt_imm() {
+    static_assert(N >= 0 && N < 64, "vmcnt is six bits");
+    return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8);
+}
 
-// Stage chunk kc of the tile's rows into an LDS buffer: 32 direct loads of
-// one KiB (4 rows x 256 bytes) per workgroup, 4 per wave.  Rows past the
-// tile's valid rows re-read the last valid row (in bounds; never stored).
-__device__ __forceinline__ void stage_chunk(const uint8_t* X, size_t xstride, int row0, int nvalid, int kc,
-                                            uint8_t* buf, int wv, int lane) {
+// Workgroup barrier for the ring.  __syncthreads() (and even an LDS-only
+// fence) makes the compiler drain every load in flight -- the next chunk's
+// included -- at each barrier.  Here each wave has already waited for its
+// own direct loads (counted vmcnt) and for its own LDS reads (their values
+// feed MFMAs issued before the barrier), so the bare barrier suffices; the
+// scheduling barriers keep the compiler from moving memory operations across.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+struct Ring {
+    uint8_t* x;  // CHUNK_LDS bytes: the token chunk
+    float* s;    // fp8: [128 rows][2 blocks] activation scales of the chunk
+};
+
+// Request chunk kc of the tile's token rows: XLOADS direct KiB loads per wave
+// (rows past the tile's valid rows re-read the last valid row: in bounds,
+// never stored); fp8: one load of 32 activation scales per wave.
+template <int DT>
+__device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, int row0, int nvalid, int kc,
+                                            const Ring& ring, int wv, int lane) {
 #pragma unroll
-    for (int i = 0; i < 32 / NW; ++i) {
-        const int q = wv * (32 / NW) + i;  // instruction index: LDS bytes [q*1024, q*1024+1024)
+    for (int i = 0; i < XLOADS; ++i) {
+        const int q = wv * XLOADS + i;     // LDS bytes [q*1024, q*1024+1024)
         const int r = q * 4 + lane / 16;   // tile row of this lane's 16 bytes
         const int slot = lane % 16;
         const int c = slot ^ (r & 15);     // source piece for this slot
         const int rr = r < nvalid ? r : nvalid - 1;
-        const uint8_t* src = X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(buf + q * 1024), 16, 0, 0);
+        const uint8_t* src = a.X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.x + q * 1024), 16, 0, 0);
+    }
+    if (DT == RDG_FP8_E4M3) {
+        // lanes 0..31 of wave w: rows 16w + l/2, scale block 2kc + l%2
+        const int r = wv * 16 + (lane & 31) / 2;
+        const int rr = r < nvalid ? r : nvalid - 1;
+        const float* src = a.Xs + (size_t)(row0 + rr) * nkb + 2 * kc + (lane & 1);
+        if (lane < 32) __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.s + wv * 32), 4, 0, 0);
     }
 }
 
-// Wave roles: gated -- wave w accumulates matrix w/4 (W1 for the gate, W3 for
-// the up projection) for columns [32(w%4), +32) over all 128 tile rows;
-// not gated -- wave w covers columns [32(w%4), +32) for tile rows [64(w/4), +64).
 template <int DT, bool GATED, bool SIGNAL>
 __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     using O = TOp<DT>;
     using op_t = typename O::op_t;
     constexpr int S = O::STEPS;
-    constexpr int NCT = GATED ? 8 : 4;  // 16-row column tiles per wave
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2][CHUNK_LDS];
+    constexpr bool FP8 = DT == RDG_FP8_E4M3;
+    __shared__ __attribute__((aligned(16))) uint8_t lx0[CHUNK_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t lx1[CHUNK_LDS];
+    __shared__ __attribute__((aligned(16))) float ls0[FP8 ? TB * 2 : 4];
+    __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * 2 : 4];
+    const Ring ring[2] = {{lx0, ls0}, {lx1, ls1}};
 
     // XCD-aware renumbering: hardware block b runs on XCD b % 8, which gets
     // ceil((total - x) / 8) blocks; give XCD x the contiguous logical range
@@ -150,92 +215,102 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * TB;
     const int row_end = a.offsets[e] + a.masked_m[e];
     const int nvalid = row_end - row0 < TB ? row_end - row0 : TB;
-    const int f0 = fb * 128;
-    const int wv = threadIdx.x / kWave, lane = lane_id();
-    const int fq = wv % 4;                      // column group
-    const int mat = GATED ? wv / 4 : 0;         // 0: W1 / W2, 1: W3
-    const int tr0 = GATED ? 0 : (wv / 4) * 64;  // first tile row of this wave
-    const int fw = f0 + fq * 32;
+    const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
+    const int lane = lane_id();
+    // gated: 128 output features per workgroup, wave w: matrix w/4, features
+    // [f0 + 32(w%4), +32); down: 256 output columns, wave w: [f0 + 32w, +32)
+    const int f0 = fb * (GATED ? PANEL / 2 : PANEL);
+    const int mat = GATED ? wv / 4 : 0;
+    const int fw = f0 + (GATED ? (wv % 4) : wv) * 32;
     const size_t xstride = (size_t)a.Kdim * O::ESZ;
     const int nks = a.Kdim / O::KS;
+    const int nkb = a.Kdim / 128;
     const int nchunks = (int)(xstride / CB);
 
-    const uint8_t* wt[2];
+    const uint8_t* wt[NRT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < NRT; ++rt) {
         const size_t grp = (size_t)e * (a.Nout / 16) + (fw + rt * 16) / 16;
         wt[rt] = (mat == 0 ? a.Wa : a.Wb) + grp * nks * O::BLK;
     }
-    f32x4_t acc[2][NCT];
+    // fp8: this wave's weight block scales along K (its 32 rows lie in one 128-row block)
+    const float* wsc = nullptr;
+    if (FP8) wsc = (mat == 0 ? a.Was : a.Wbs) + ((size_t)e * (a.Nout / 128) + fw / 128) * nkb;
+
+    f32x4_t acc[NRT][NCT];
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int nkb = a.Kdim / 128;
-    const float* wsc = nullptr;  // this wave's weight block scales along K
-    if (DT == RDG_FP8_E4M3) wsc = (mat == 0 ? a.Was : a.Wbs) + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
+    // two weight register sets (chunk k's and k+1's), three ring slots
+    op_t w[2][S][NRT];
+    float sw[2][S];
 
-    // prologue: chunk 0 into buffer 0; weights into registers (bf16: the whole
-    // first chunk, fp8: the first step)
-    stage_chunk(a.X, xstride, row0, nvalid, 0, lds[0], wv, lane);
-    constexpr int WS = DT == RDG_FP8_E4M3 ? 1 : S;  // weight steps held per register set
-    op_t wreg[WS][2];
+    auto request_w = [&](int kc, op_t (&wr)[S][NRT], float (&swr)[S]) {
+        O::load_w(wr, wt, kc * S, lane);
+        if (FP8) {
 #pragma unroll
-    for (int s = 0; s < WS; ++s)
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) wreg[s][rt] = O::load_w(wt[rt] + (size_t)s * O::BLK, lane);
-
-    for (int kc = 0; kc < nchunks; ++kc) {
-        uint8_t* cur = lds[kc & 1];
-        __builtin_amdgcn_s_waitcnt(0);  // this wave's share of chunk kc (and its weights) have landed
-        __syncthreads();                // ... and every wave's share; buffer kc+1 is free again
-        if (kc + 1 < nchunks) stage_chunk(a.X, xstride, row0, nvalid, kc + 1, lds[(kc + 1) & 1], wv, lane);
-        op_t wnext[WS][2];
-        if (DT != RDG_FP8_E4M3 && kc + 1 < nchunks) {
-#pragma unroll
-            for (int s = 0; s < WS; ++s)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) wnext[s][rt] = O::load_w(wt[rt] + (size_t)((kc + 1) * S + s) * O::BLK, lane);
+            for (int s = 0; s < S; ++s) swr[s] = wsc[kc * S + s];
         }
+    };
+    auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT], const float (&swr)[S]) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const int ws = DT == RDG_FP8_E4M3 ? 0 : s;
-            const int t = kc * S + s;  // global step
-            float sw = 0.0f;
-            if (DT == RDG_FP8_E4M3) {
-                if (t + 1 < nks) {  // next step's weights while this step computes
+            // one step's token operands at a time (the scheduler would
+            // otherwise hoist a whole chunk's LDS reads and run out of registers)
+            __builtin_amdgcn_sched_barrier(0);
+            if (!FP8) {
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) wnext[0][rt] = O::load_w(wt[rt] + (size_t)(t + 1) * O::BLK, lane);
+                for (int ct = 0; ct < NCT; ++ct) {
+                    const op_t xo = O::load_x(rg.x, ct * 16 + (lane & 15), s, lane >> 4);
+#pragma unroll
+                    for (int rt = 0; rt < NRT; ++rt) acc[rt][ct] = O::mma(acc[rt][ct], wr[s][rt], xo);
                 }
-                sw = wsc[t];
-            }
-            // one column tile's token operand at a time
+            } else {
+                // the block partials of token tile ct are promoted while the
+                // MFMAs of tile ct+1 run (two partial sets live at a time)
+                f32x4_t p[2][NRT];
+                float f[2];
+                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const op_t xo = O::load_x(cur, tr0 + ct * 16 + (lane & 15), s, lane >> 4);
-                if (DT != RDG_FP8_E4M3) {
+                for (int ct = 0; ct <= NCT; ++ct) {
+                    if (ct < NCT) {
+                        const int r = ct * 16 + (lane & 15);
+                        const op_t xo = O::load_x(rg.x, r, s, lane >> 4);
+                        f[ct % 2] = rg.s[r * 2 + s] * swr[s];
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) acc[rt][ct] = O::mma(acc[rt][ct], wreg[ws][rt], xo);
-                } else {
-                    // one MFMA per 128-long block, promoted with its activation and weight scales
-                    const int r = tr0 + ct * 16 + (lane & 15);
-                    const float sx = a.Xs[(size_t)(row0 + (r < nvalid ? r : nvalid - 1)) * nkb + t];
-                    const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+                        for (int rt = 0; rt < NRT; ++rt) p[ct % 2][rt] = O::mma(z, wr[s][rt], xo);
+                    }
+                    if (ct > 0) {
 #pragma unroll
-                    for (int rt = 0; rt < 2; ++rt) acc[rt][ct] += O::mma(z, wreg[0][rt], xo) * (sx * sw);
+                        for (int rt = 0; rt < NRT; ++rt) acc[rt][ct - 1] += p[(ct - 1) % 2][rt] * f[(ct - 1) % 2];
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-            if (DT == RDG_FP8_E4M3 && t + 1 < nks) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) wreg[0][rt] = wnext[0][rt];
             }
         }
-        if (DT != RDG_FP8_E4M3 && kc + 1 < nchunks) {
+    };
+
+    // Chunk k+1's token rows and weights are requested once chunk k has
+    // arrived, and are in flight while chunk k is multiplied.
+    stage_chunk<DT>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+    request_w(0, w[0], sw[0]);
+    for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
 #pragma unroll
-            for (int s = 0; s < WS; ++s)
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt) wreg[s][rt] = wnext[s][rt];
+        for (int j = 0; j < 2; ++j) {
+            const int kc = kc0 + j;
+            if (kc >= nchunks) break;
+            // this wave's loads of chunk kc have landed, then every wave's; past
+            // the barrier every wave is also done with chunk kc-1, whose ring
+            // slot and weight set are refilled next
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+            lds_barrier();
+            if (kc + 1 < nchunks) {
+                stage_chunk<DT>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
+                request_w(kc + 1, w[(j + 1) % 2], sw[(j + 1) % 2]);
+            }
+            compute(ring[j], w[j], sw[j]);
         }
     }
 
@@ -243,47 +318,51 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // 16x16 accumulator tile: lane l holds column (row of the layout) l % 16 and
     // rows (output features) 4*(l/16) .. +3
     const int fl = fw + (lane >> 4) * 4;
+    __syncthreads();  // every wave is done with the ring
     if (GATED) {
-        // the up-projection waves hand their accumulators to the gate waves
-        __syncthreads();  // every wave is done with the staging buffers
-        f32x4_t* xch = reinterpret_cast<f32x4_t*>(lds[0]);  // [4 column groups][2][8][64 lanes] = 64 KiB
+        // the up-projection waves hand their accumulators to the gate waves,
+        // weight tile rt through ring slot rt: [4 feature groups][8][64 lanes]
         if (mat == 1) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < NRT; ++rt) {
+                f32x4_t* xch = reinterpret_cast<f32x4_t*>(rt == 0 ? lx0 : lx1);
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) xch[((fq * 2 + rt) * 8 + ct) * kWave + lane] = acc[rt][ct];
+                for (int ct = 0; ct < NCT; ++ct) xch[((wv % 4) * NCT + ct) * kWave + lane] = acc[rt][ct];
+            }
         }
         __syncthreads();
         if (mat == 0) {
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt)
+            for (int rt = 0; rt < NRT; ++rt) {
+                const f32x4_t* xch = reinterpret_cast<const f32x4_t*>(rt == 0 ? lx0 : lx1);
 #pragma unroll
                 for (int ct = 0; ct < NCT; ++ct) {
-                    const f32x4_t u = xch[((fq * 2 + rt) * 8 + ct) * kWave + lane];
+                    const f32x4_t u = xch[((wv % 4) * NCT + ct) * kWave + lane];
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
                         const float g = acc[rt][ct][r];
                         acc[rt][ct][r] = g / (1.0f + __expf(-g)) * u[r];
                     }
                 }
+            }
         }
-        __syncthreads();  // the exchange area is free again
     }
-    if (DT == RDG_FP8_E4M3 && GATED) {
-        // h re-quantised with one fp32 scale per row and 128 columns: amax over
-        // the four gate waves' 32 columns each
-        float* red = reinterpret_cast<float*>(lds[0]);  // [4 column groups][128 rows]
+    if (FP8 && GATED) {
+        // h re-quantised with one fp32 scale per row and 128 features: amax
+        // over the four gate waves' 32 features each
+        __syncthreads();                              // the exchange area is read
+        float* red = reinterpret_cast<float*>(lx0);  // [4 feature groups][128 rows]
         if (mat == 0) {
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
                 float m = 0.0f;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
+                for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[rt][ct][r]));
                 m = fmaxf(m, __shfl_xor(m, 16));
                 m = fmaxf(m, __shfl_xor(m, 32));
-                if (lane < 16) red[fq * TB + ct * 16 + lane] = m;
+                if (lane < 16) red[(wv % 4) * TB + ct * 16 + lane] = m;
             }
         }
         __syncthreads();
@@ -297,7 +376,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
                 const float inv = 1.0f / sc;
 #pragma unroll
-                for (int rt = 0; rt < 2; ++rt) {
+                for (int rt = 0; rt < NRT; ++rt) {
                     uint32_t q = 0;
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
@@ -306,17 +385,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                     }
                     *reinterpret_cast<uint32_t*>(a.O + (size_t)row * a.Nout + fl + rt * 16) = q;
                 }
-                if (fq == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = sc;
+                if (wv == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = sc;
             }
         }
     } else if (mat == 0) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-            const int c = tr0 + ct * 16 + (lane & 15);
+            const int c = ct * 16 + (lane & 15);
             if (c >= nvalid) continue;
             const int row = row0 + c;
 #pragma unroll
-            for (int rt = 0; rt < 2; ++rt) {
+            for (int rt = 0; rt < NRT; ++rt) {
                 uint2 o;
                 o.x = f32_to_bf16(acc[rt][ct][0]) | (f32_to_bf16(acc[rt][ct][1]) << 16);
                 o.y = f32_to_bf16(acc[rt][ct][2]) | (f32_to_bf16(acc[rt][ct][3]) << 16);
@@ -328,7 +407,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         __threadfence();
         __syncthreads();
         if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / TB, 128, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_add(a.signals + row0 / TB, PANEL, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -339,7 +418,7 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
         TArgs g{c.offsets, c.masked_m, c.tile_off, c.n_local, c.H, c.I, c.n_tiles_max,
                 static_cast<const uint8_t*>(c.x), c.x_s, static_cast<const uint8_t*>(c.W1),
                 static_cast<const uint8_t*>(c.W3), c.W1_s, c.W3_s, static_cast<uint8_t*>(c.h), c.h_s, nullptr};
-        k_ffn_tiled<DT, true, false><<<dim3(c.n_tiles_max, c.I / 128), block, 0, s>>>(g);
+        k_ffn_tiled<DT, true, false><<<dim3(c.n_tiles_max, c.I / (PANEL / 2)), block, 0, s>>>(g);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -348,17 +427,27 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
                 static_cast<const uint8_t*>(c.h), c.h_s, static_cast<const uint8_t*>(c.W2), nullptr, c.W2_s,
                 nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
         if (c.signals)
-            k_ffn_tiled<DT, false, true><<<dim3(c.n_tiles_max, c.H / 128), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, true><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
         else
-            k_ffn_tiled<DT, false, false><<<dim3(c.n_tiles_max, c.H / 128), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, false><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
     }
     return hipGetLastError();
 }
 
 }  // namespace
 
+// bf16 / fp8 with I a multiple of 128 (the gate/up feature panel) and H a
+// multiple of 256 (the down column panel); both reduction dimensions in whole
+// 256-byte chunks.
+bool tiled_supported(int dtype, int H, int I) {
+    const int esz = dtype == RDG_BF16 ? 2 : dtype == RDG_FP8_E4M3 ? 1 : 0;
+    return esz > 0 && I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * esz) % CB == 0 &&
+           ((int64_t)I * esz) % CB == 0;
+}
+
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s) {
     if (c.n_tiles_max <= 0) return hipSuccess;
+    if (!tiled_supported(c.dtype, c.H, c.I)) return hipErrorInvalidValue;
     if (c.dtype == RDG_BF16) return launch_dt<RDG_BF16>(c, s);
     if (c.dtype == RDG_FP8_E4M3) return launch_dt<RDG_FP8_E4M3>(c, s);
     return hipErrorInvalidValue;

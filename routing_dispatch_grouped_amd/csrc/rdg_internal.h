@@ -136,6 +136,7 @@ struct FfnCall {
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s);  // bt == 128, bf16 / fp8
+bool tiled_supported(int dtype, int H, int I);                 // shapes the bt == 128 kernels take
 
 hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
                           const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
