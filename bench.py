@@ -217,6 +217,7 @@ class Bench:
             self.signals = torch.zeros(((self.L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=self.dev)
             self.threshold = rdg.rdg_signal_threshold(cfg["H"], self.DT)
             self.side = torch.cuda.Stream()
+            self.gate_done = torch.cuda.Event()
         if cfg.get("shared_I"):
             self.x_own, self.x_own_s = self._quant(synth.x(cfg, cfg["own_tokens"], device=self.dev, tensor=10))
             self.Wsh, self.Ssh = self._experts([0], shared=True)
@@ -261,16 +262,20 @@ class Bench:
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
             return
-        # signalled down GEMM on this stream; shared expert + polling combine on the side stream
+        # signalled down GEMM on this stream; on the side stream the shared
+        # expert (overlapping gate/up), then the polling combine, released once
+        # gate/up is done so that it overlaps the down GEMM
         rdg.rdg_fill_i32(self.signals, 0)
         self.side.wait_stream(self.stream)
         self._gate_up(timed)
+        self.gate_done.record(self.stream)
         rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y,
                              self.signals)
         with self.torch.cuda.stream(self.side):
             self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
+            self.side.wait_event(self.gate_done)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
-                            self.signal_rows, self.threshold, 1_000_000, 64, stream=self.side)
+                            self.signal_rows, self.threshold, 1_000_000, 256, stream=self.side)
         self.stream.wait_stream(self.side)
 
 

@@ -200,7 +200,9 @@ int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h
 
 /* Rows per signal counter (the grouped GEMMs' row tile for this layout,
  * type and size: 16, 32, 64 or 128) and the counter value that means "row
- * tile done" (H), for the down GEMM of rdg_grouped_ffn. */
+ * tile done" (H), for the down GEMM of rdg_grouped_ffn.  With signals, the
+ * down GEMM runs its workgroups tile-major, so row tiles complete in layout
+ * order; at most 65535 row tiles (RDG_EUNSUPPORTED beyond). */
 int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I);
 int rdg_signal_threshold(int H, int dtype);
 
@@ -219,11 +221,15 @@ int rdg_signal_threshold(int H, int dtype);
  *              threshold and a timeout in microseconds (a tile still
  *              incomplete then is skipped and status = RDG_ETIMEOUT with
  *              detail = the tile index)
- *   max_blocks 0 = one wavefront per token; else at most this many 256-thread
- *              workgroups loop over the tokens (keeps a polling combine from
- *              occupying the CUs the down GEMM needs).
+ *   max_blocks 0 = one wavefront per token and 512-feature slice; else at
+ *              most this many 256-thread workgroups loop over the work (keeps
+ *              a polling combine from occupying the CUs the down GEMM needs).
  * The polling form may run on another stream concurrently with the down
- * GEMM, which must have been enqueued first. */
+ * GEMM, which must have been enqueued first.  It visits the tokens in the
+ * order their rows become ready -- each token at its last layout row,
+ * walking L->row_src in layout order, which is the order the signalled down
+ * GEMM completes its row tiles -- and then the tokens with no local row, so
+ * L->row_src must be set.  The output does not depend on the visiting order. */
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
                 const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
                 int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream);

@@ -167,6 +167,7 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     if (signals) {
         const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
         if (align % bt != 0) return RDG_EUNSUPPORTED;
+        if (ffn_tiles_max(L, bt) > 65535) return RDG_EUNSUPPORTED;  // row tiles on grid y
     }
     FfnCall c{};
     c.offsets = L->offsets;
@@ -230,13 +231,13 @@ int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* to
     int rows_per_sig = 1;
     uint64_t ticks = 0;
     if (signals) {
-        if (threshold < 1 || timeout_us < 0 || !L->status) return RDG_EINVAL;
+        if (threshold < 1 || timeout_us < 0 || !L->status || !L->row_src) return RDG_EINVAL;
         if (signal_rows != 16 && signal_rows != 32 && signal_rows != 64 && signal_rows != 128) return RDG_EINVAL;
         rows_per_sig = signal_rows;
         ticks = (uint64_t)timeout_us * wall_ticks_per_us();
     }
-    return hip_rc(launch_combine(y, y_dtype, L->pos, topk_w, T, K, H, shared_out, out, out_dtype, signals,
-                                 rows_per_sig, threshold, ticks, max_blocks, L->status, stream));
+    return hip_rc(launch_combine(y, y_dtype, L->pos, L->row_src, L->m_cap, topk_w, T, K, H, shared_out, out,
+                                 out_dtype, signals, rows_per_sig, threshold, ticks, max_blocks, L->status, stream));
 }
 
 int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,

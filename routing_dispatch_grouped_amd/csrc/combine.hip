@@ -13,10 +13,11 @@
 // Design for CDNA4: one wave per (token, 512-feature slice); each lane owns
 // 8 consecutive features (a 16-byte bf16 vector), gathers the K expert rows
 // for them, accumulates in fp32 and writes once.  Slicing the row keeps a
-// 128-token decode batch from occupying only a handful of CUs.  In the polling form, lane 0
-// waits (acquire, device scope) on the counter of each row tile the token
-// reads; a bounded wait turns a tile that never completes into a status
-// code instead of a hang.
+// 128-token decode batch from occupying only a handful of CUs.  In the
+// polling form, tokens are visited in the order their rows become ready (see
+// k_combine), and lane 0 waits (acquire, device scope) on the counter of each
+// row tile the token reads; a bounded wait turns a tile that never completes
+// into a status code instead of a hang.
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -61,13 +62,98 @@ __device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_t
     const uint64_t t0 = wall_clock64();
     while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < threshold) {
         if (wall_clock64() - t0 > timeout_ticks) return false;
-        __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_s_sleep(8);  // ~500 cycles: keeps the polling traffic on the counters' L2 lines low
     }
     return true;
 }
 
+__device__ __forceinline__ int wave_max_i32(int v) {
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o));
+    return v;
+}
+
+// READY (polling form): tokens are visited in the order their rows become
+// ready -- token t at its last layout row max_k pos[t,k], walking the layout
+// rows in order, which is the order the signalled down GEMM completes its row
+// tiles -- and then the tokens with no row on this GPU.  Otherwise tokens are
+// visited in index order.
+// Token t's slots into this wave's LDS row: positions (-1: no row, or a row
+// whose tile never completed) and weights.  Polling form: lane 0 first waits
+// for the counter of every row tile the token reads, then one acquire makes
+// the rows' values visible.
+__device__ __forceinline__ void token_slots(const int32_t* __restrict__ pos, const float* __restrict__ w, int t,
+                                            int K, const int32_t* signals, int rows_per_sig, int threshold,
+                                            uint64_t timeout_ticks, int32_t* status, int* pos_l, float* w_l,
+                                            int lane) {
+    int p = -1;
+    float wt = 0.0f;
+    if (lane < K) {
+        p = pos[(size_t)t * K + lane];
+        wt = w[(size_t)t * K + lane];
+    }
+    if (signals != nullptr) {
+        for (int k = 0; k < K; ++k) {
+            const int pk = __shfl(p, k);
+            if (pk < 0) continue;
+            int ok = 1;
+            if (lane == 0) {
+                ok = wait_counter(signals + pk / rows_per_sig, threshold, timeout_ticks) ? 1 : 0;
+                if (!ok) set_status(status, RDG_ETIMEOUT, pk / rows_per_sig);
+            }
+            ok = __shfl(ok, 0);
+            if (!ok && lane == k) p = -1;  // skip the incomplete row
+        }
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    // the feature loop may leave lanes idle: it reads the slots from LDS
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < K) {
+        pos_l[lane] = p;
+        w_l[lane] = wt;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One 512-feature slice of token t: lane l owns features [8v, 8v+8), v = 64*slice + l.
 template <int YDT, int ODT>
+__device__ __forceinline__ void combine_slice(const void* __restrict__ y, const void* __restrict__ shared_out,
+                                              void* __restrict__ out, int t, int slice, int K, int H,
+                                              const int* pos_l, const float* w_l, int lane) {
+    const int v = slice * kWave + lane;
+    if (v >= H / 8) return;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < K; ++k) {
+        const int pk = pos_l[k];
+        const float wk = w_l[k];
+        if (pk < 0) continue;
+        float yv[8];
+        load8<YDT>(y, (size_t)pk, H, v, yv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += wk * yv[i];
+    }
+    if (shared_out != nullptr) {
+        float sv[8];
+        load8<ODT>(shared_out, (size_t)t, H, v, sv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] += sv[i];
+    }
+    store8<ODT>(out, (size_t)t, H, v, acc);
+}
+
+// Plain form: one wave per (token, 512-feature slice) unit, tokens in index
+// order.  Polling form (READY): one wave per token, visited in the order its
+// rows become ready -- token t at its last layout row max_k pos[t,k], walking
+// the layout rows in order, which is the order the signalled down GEMM
+// completes its row tiles -- then the tokens with no row on this GPU; the
+// wave polls once for the token and then combines all of its slices.
+template <int YDT, int ODT, bool READY>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ pos,
+                                                 const int32_t* __restrict__ row_src, int m_cap,
                                                  const float* __restrict__ w, int T, int K, int H,
                                                  const void* __restrict__ shared_out, void* __restrict__ out,
                                                  const int32_t* signals, int rows_per_sig, int threshold,
@@ -75,77 +161,61 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
     __shared__ int pos_lds[4][32];
     __shared__ float w_lds[4][32];
     const int wv = threadIdx.x / kWave, lane = lane_id();
-    const int nvec = H / 8;
-    const int n_slices = (nvec + kWave - 1) / kWave;
-    const int64_t n_units = (int64_t)T * n_slices;
-    for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += (int64_t)gridDim.x * 4) {
-        const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
-        int p = -1;
-        float wt = 0.0f;
-        if (lane < K) {
-            p = pos[(size_t)t * K + lane];
-            wt = w[(size_t)t * K + lane];
+    const int n_slices = (H / 8 + kWave - 1) / kWave;
+    const int64_t stride = (int64_t)gridDim.x * 4;
+    if (!READY) {
+        const int64_t n_units = (int64_t)T * n_slices;
+        for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += stride) {
+            const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
+            token_slots(pos, w, t, K, nullptr, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv],
+                        w_lds[wv], lane);
+            combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
         }
-        if (signals != nullptr) {
-            for (int k = 0; k < K; ++k) {
-                const int pk = __shfl(p, k);
-                if (pk < 0) continue;
-                int ok = 1;
-                if (lane == 0) {
-                    ok = wait_counter(signals + pk / rows_per_sig, threshold, timeout_ticks) ? 1 : 0;
-                    if (!ok) set_status(status, RDG_ETIMEOUT, pk / rows_per_sig);
-                }
-                ok = __shfl(ok, 0);
-                if (!ok && lane == k) p = -1;  // skip the incomplete row
-            }
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        return;
+    }
+    const int64_t n_units = (int64_t)m_cap + T;
+    for (int64_t u0 = (int64_t)blockIdx.x * 4 + wv; u0 < n_units; u0 += stride) {
+        int t;
+        if (u0 < m_cap) {
+            const int src = row_src[u0];  // wave-uniform
+            if (src < 0) continue;        // padding row
+            t = src / K;
+            const int last = wave_max_i32(lane < K ? pos[(size_t)t * K + lane] : -1);
+            if (last != (int)u0) continue;  // the token is combined at its last row
+        } else {
+            t = (int)(u0 - m_cap);
+            const int last = wave_max_i32(lane < K ? pos[(size_t)t * K + lane] : -1);
+            if (last >= 0) continue;  // combined at its last row above
         }
-        // the feature loop below may leave lanes idle: read the slots from LDS
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        if (lane < K) {
-            pos_lds[wv][lane] = p;
-            w_lds[wv][lane] = wt;
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        const int v = slice * kWave + lane;
-        if (v < nvec) {
-            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            for (int k = 0; k < K; ++k) {
-                const int pk = pos_lds[wv][k];
-                const float wk = w_lds[wv][k];
-                if (pk < 0) continue;
-                float yv[8];
-                load8<YDT>(y, (size_t)pk, H, v, yv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += wk * yv[i];
-            }
-            if (shared_out != nullptr) {
-                float sv[8];
-                load8<ODT>(shared_out, (size_t)t, H, v, sv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[i] += sv[i];
-            }
-            store8<ODT>(out, (size_t)t, H, v, acc);
-        }
+        token_slots(pos, w, t, K, signals, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv], w_lds[wv],
+                    lane);
+        for (int slice = 0; slice < n_slices; ++slice)
+            combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
     }
 }
 
 }  // namespace
 
-hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
-                          const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
-                          int threshold, uint64_t timeout_ticks, int max_blocks, int32_t* status, hipStream_t s) {
+hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int32_t* row_src, int m_cap,
+                          const float* w, int T, int K, int H, const void* shared_out, void* out, int out_dt,
+                          const int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
+                          int max_blocks, int32_t* status, hipStream_t s) {
     if (T == 0) return hipSuccess;
-    const int64_t units = (int64_t)T * ((H / 8 + kWave - 1) / kWave);
+    const bool ready = signals != nullptr;
+    const int64_t units = ready ? (int64_t)m_cap + T : (int64_t)T * ((H / 8 + kWave - 1) / kWave);
     int64_t blocks = (units + 3) / 4;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
-#define RDG_COMBINE(YD, OD)                                                                                     \
-    k_combine<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, signals, rows_per_sig,        \
-                                              threshold, timeout_ticks, status)
+#define RDG_COMBINE(YD, OD)                                                                                    \
+    do {                                                                                                       \
+        if (ready)                                                                                             \
+            k_combine<YD, OD, true><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,        \
+                                                                   shared_out, out, signals, rows_per_sig,    \
+                                                                   threshold, timeout_ticks, status);         \
+        else                                                                                                   \
+            k_combine<YD, OD, false><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,       \
+                                                                    shared_out, out, nullptr, rows_per_sig,   \
+                                                                    threshold, timeout_ticks, status);        \
+    } while (0)
     if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_COMBINE(RDG_BF16, RDG_BF16);
     else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_COMBINE(RDG_BF16, RDG_F32);
     else if (y_dt == RDG_F32 && out_dt == RDG_F32) RDG_COMBINE(RDG_F32, RDG_F32);

@@ -139,7 +139,9 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
     // output storage: fp32 layer -> fp32; bf16 -> bf16; fp8: h in e4m3, y in bf16
     constexpr int OUT_KIND = DT == RDG_F32 ? 0 : (DT == RDG_FP8_E4M3 && GATED) ? 2 : 1;
 
-    const int tile = blockIdx.x;
+    // signalled: tile-major order (grid x = column block), so that row tiles
+    // complete in layout order for the polling consumer
+    const int tile = SIGNAL ? blockIdx.y : blockIdx.x;
     const int n_tiles = a.tile_off[a.n_local];
     if (tile >= n_tiles) return;  // workgroup-uniform
     int lo = 0, hi = a.n_local;
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
     const int e = lo;
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
-    const int f0 = blockIdx.y * 128;
+    const int f0 = (SIGNAL ? blockIdx.x : blockIdx.y) * 128;
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int fw = f0 + wv * 32;
     const size_t wstride = (size_t)a.Kdim * ESZ;
@@ -355,7 +357,9 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     static_assert(DT == RDG_FP8_E4M3 || 128 % (KS * U) == 0, "KS * U must divide 128");
     __shared__ f32x4_t part[4][FPW * G * NR][kWave];
 
-    const int tile = blockIdx.x;
+    // signalled: tile-major order (grid x = column block), so that row tiles
+    // complete in layout order for the polling consumer
+    const int tile = SIGNAL ? blockIdx.y : blockIdx.x;
     const int n_tiles = a.tile_off[a.n_local];
     if (tile >= n_tiles) return;  // workgroup-uniform
     int lo = 0, hi = a.n_local;
@@ -367,7 +371,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     const int e = lo;
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
-    const int f0 = blockIdx.y * (16 * FPW);
+    const int f0 = (SIGNAL ? blockIdx.x : blockIdx.y) * (16 * FPW);
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const size_t wstride = (size_t)a.Kdim * ESZ;
 
@@ -566,11 +570,10 @@ hipError_t launch_skinny(const FfnCall& c, hipStream_t s) {
     }
     if (c.stages & 2) {
         const KArgs d = down_args(c);
-        const dim3 grid2(c.n_tiles_max, c.H / 32);
         if (c.signals)
-            k_ffn_skinny<DT, false, true, 2, NR><<<grid2, block, 0, s>>>(d);
+            k_ffn_skinny<DT, false, true, 2, NR><<<dim3(c.H / 32, c.n_tiles_max), block, 0, s>>>(d);
         else
-            k_ffn_skinny<DT, false, false, 2, NR><<<grid2, block, 0, s>>>(d);
+            k_ffn_skinny<DT, false, false, 2, NR><<<dim3(c.n_tiles_max, c.H / 32), block, 0, s>>>(d);
     }
     return hipGetLastError();
 }
@@ -586,11 +589,10 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     }
     if (c.stages & 2) {
         const KArgs d = down_args(c);
-        const dim3 grid2(c.n_tiles_max, c.H / 128);
         if (c.signals)
-            k_ffn<DT, BT, false, true><<<grid2, block, 0, s>>>(d);
+            k_ffn<DT, BT, false, true><<<dim3(c.H / 128, c.n_tiles_max), block, 0, s>>>(d);
         else
-            k_ffn<DT, BT, false, false><<<grid2, block, 0, s>>>(d);
+            k_ffn<DT, BT, false, false><<<dim3(c.n_tiles_max, c.H / 128), block, 0, s>>>(d);
     }
     return hipGetLastError();
 }

@@ -35,7 +35,9 @@
 // the fp32 accumulator with its activation and weight scales.
 //
 // Workgroups are renumbered so that the token tiles sharing one weight panel
-// run back to back on the same XCD and re-read the panel from its L2.
+// run back to back on the same XCD and re-read the panel from its L2; the
+// signalled down stage instead runs tile-major, so that row tiles complete in
+// layout order while a combine polls them.
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -193,15 +195,25 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * 2 : 4];
     const Ring ring[2] = {{lx0, ls0}, {lx1, ls1}};
 
-    // XCD-aware renumbering: hardware block b runs on XCD b % 8, which gets
-    // ceil((total - x) / 8) blocks; give XCD x the contiguous logical range
-    // starting at x*(total/8) + min(x, total%8) (a bijection for any total), so
-    // consecutive row tiles of one weight panel share an L2
-    const int gx = a.n_tiles_max, total = gx * gridDim.y;
-    const int b = blockIdx.y * gx + blockIdx.x;
-    const int xcd = b % 8, q8 = total / 8, r8 = total % 8;
-    const int logical = xcd * q8 + (xcd < r8 ? xcd : r8) + b / 8;
-    const int fb = logical / gx, tile = logical % gx;
+    int fb, tile;
+    if (SIGNAL) {
+        // tile-major in dispatch order (grid x = column panel): row tiles
+        // complete in layout order for the polling consumer; XCD x then runs
+        // the panels fb = x (mod 8) of every tile and keeps them in its L2
+        fb = blockIdx.x;
+        tile = blockIdx.y;
+    } else {
+        // XCD-aware renumbering: hardware block b runs on XCD b % 8, which
+        // gets ceil((total - x) / 8) blocks; give XCD x the contiguous logical
+        // range starting at x*(total/8) + min(x, total%8) (a bijection for any
+        // total), so consecutive row tiles of one weight panel share an L2
+        const int gx = a.n_tiles_max, total = gx * gridDim.y;
+        const int b = blockIdx.y * gx + blockIdx.x;
+        const int xcd = b % 8, q8 = total / 8, r8 = total % 8;
+        const int logical = xcd * q8 + (xcd < r8 ? xcd : r8) + b / 8;
+        fb = logical / gx;
+        tile = logical % gx;
+    }
 
     const int n_tiles = a.tile_off[a.n_local];
     if (tile >= n_tiles) return;  // workgroup-uniform
@@ -427,7 +439,7 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
                 static_cast<const uint8_t*>(c.h), c.h_s, static_cast<const uint8_t*>(c.W2), nullptr, c.W2_s,
                 nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
         if (c.signals)
-            k_ffn_tiled<DT, false, true><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, true><<<dim3(c.H / PANEL, c.n_tiles_max), block, 0, s>>>(d);
         else
             k_ffn_tiled<DT, false, false><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
     }

@@ -138,8 +138,9 @@ hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s);  // bt == 128, bf16 / fp8
 bool tiled_supported(int dtype, int H, int I);                 // shapes the bt == 128 kernels take
 
-hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const float* w, int T, int K, int H,
-                          const void* shared_out, void* out, int out_dt, const int32_t* signals, int rows_per_sig,
-                          int threshold, uint64_t timeout_ticks, int max_blocks, int32_t* status, hipStream_t s);
+hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int32_t* row_src, int m_cap,
+                          const float* w, int T, int K, int H, const void* shared_out, void* out, int out_dt,
+                          const int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
+                          int max_blocks, int32_t* status, hipStream_t s);
 
 }  // namespace rdg

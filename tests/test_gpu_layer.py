@@ -273,6 +273,58 @@ def test_prefill_rank_fp8_workload_sbo():
     assert err <= tolerance(cfg)
 
 
+# Signalled down GEMM + concurrently polling combine on a small rank share:
+# experts 8..15 of 32 are local, so many tokens have no local row (combined
+# in the combine's second pass); the rows per local expert (about B*4/32)
+# select 16-, 32-, 64- (fp32) and 128-row (bf16/fp8) tiles; contiguous and
+# masked layouts.  The concurrent run must equal the sequential one bit for
+# bit and the oracle within tolerance.
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("B", [40, 300, 600])
+@pytest.mark.parametrize("kind", [0, 1])
+def test_sbo_small(dtype, B, kind):
+    m = rdg()
+    cfg = _small_cfg(dtype, wid=500 + B + kind)
+    dt = dt_code(cfg)
+    logits = synth.logits(cfg, B)
+    ids, w, ri, rw = _route(cfg, logits)
+    p0, n_local = 8, 8
+    loc_np = np.where((ri >= p0) & (ri < p0 + n_local), ri - p0, -1).astype(np.int32)
+    loc = torch.from_numpy(loc_np).to(DEV)
+    x = synth.x(cfg, B, device=DEV)
+    x_s, xo, xo_s = None, np_of(x), None
+    if dtype == "fp8":
+        x, x_s = quantize_act(x)
+        xo, xo_s = oracle.quantize_fp8(xo, 1)
+    experts = ExpertSet(cfg, range(p0, p0 + n_local))
+    m_max = ((B + 127) // 128) * 128 if kind == m.RDG_MASKED else 0
+    seq = run_routed(cfg, x, x_s, loc, w, experts, kind, block_m=128, m_max=m_max)
+    sbo = run_routed(cfg, x, x_s, loc, w, experts, kind, block_m=128, m_max=m_max, signals=True, concurrent=True,
+                     max_blocks=8)
+    assert m.rdg_check_status(sbo["L"]) == (0, 0)
+    rows = sbo["signal_rows"]
+    sig, off, mm = np_of(sbo["signals"]), np_of(sbo["L"].offsets), np_of(sbo["L"].masked_m)
+    want = np.zeros_like(sig)
+    for e in range(n_local):
+        for j in range((mm[e] + rows - 1) // rows):
+            want[(off[e] + j * rows) // rows] = sbo["threshold"]
+    assert np.array_equal(sig, want)
+    orphans = int((loc_np < 0).all(1).sum())
+    ndiff = int((sbo["out"] != seq["out"]).any(1).sum())
+    print("sbo small %s B=%d kind=%d rows/signal=%d orphans=%d differing=%d" % (dtype, B, kind, rows, orphans, ndiff),
+          flush=True)
+    assert orphans > 0 and ndiff == 0
+    used = set(np.unique(loc_np[loc_np >= 0]).tolist())
+    ref = oracle.moe_layer(dt, xo, loc_np, rw, [experts.oracle_expert(j) if j in used else None
+                                                 for j in range(n_local)], x_scales=xo_s)
+    got = np_of(sbo["out"])
+    err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
+    keep = np.flatnonzero((loc_np >= 0).any(1))
+    check_rows(got[keep], ref[keep], cfg, "sbo small")
+    assert not out_as_f64(got[(loc_np < 0).all(1)]).any(), "tokens without a local row must be zero"
+    assert err <= tolerance(cfg), err
+
+
 def test_sbo_timeout_is_reported_not_hung():
     """A threshold the producer can never reach: the combine gives up after
     its timeout, flags RDG_ETIMEOUT, and every kernel still exits."""
