@@ -275,7 +275,7 @@ class Bench:
             self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             self.side.wait_event(self.gate_done)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
-                            self.signal_rows, self.threshold, 1_000_000, 256, stream=self.side)
+                            self.signal_rows, self.threshold, 1_000_000, 64, stream=self.side)
         self.stream.wait_stream(self.side)
 
 

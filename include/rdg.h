@@ -222,8 +222,11 @@ int rdg_signal_threshold(int H, int dtype);
  *              incomplete then is skipped and status = RDG_ETIMEOUT with
  *              detail = the tile index)
  *   max_blocks 0 = one wavefront per token and 512-feature slice; else at
- *              most this many 256-thread workgroups loop over the work (keeps
- *              a polling combine from occupying the CUs the down GEMM needs).
+ *              most this many 256-thread workgroups loop over the work.  The
+ *              polling form never uses more than a quarter of the GPU's CUs'
+ *              worth of workgroups (fewer if max_blocks says so): waiting
+ *              workgroups hold their CU, and the down GEMM's workgroups must
+ *              always find CUs to run on.
  * The polling form may run on another stream concurrently with the down
  * GEMM, which must have been enqueued first.  It visits the tokens in the
  * order their rows become ready -- each token at its last layout row,

@@ -41,6 +41,33 @@ __device__ __forceinline__ void load8(const void* y, size_t row, int H, int v, f
     }
 }
 
+// load8 for rows published by a concurrently running producer on another
+// XCD: device-scope (relaxed atomic) loads, which read past this CU's L1 and
+// any stale line of this XCD's L2 -- so the consumer needs no device-scope
+// acquire, whose L2 invalidation would hurt the producer's workgroups here.
+template <int YDT>
+__device__ __forceinline__ void load8_published(const void* y, size_t row, int H, int v, float* out) {
+    if (YDT == RDG_BF16) {
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const uint16_t*>(y) + row * H) + 2 * v;
+        const uint64_t lo = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t hi = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t w[4] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            out[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+            out[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+        }
+    } else {
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const float*>(y) + row * H) + 4 * v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint64_t q = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            out[2 * i] = __uint_as_float((uint32_t)q);
+            out[2 * i + 1] = __uint_as_float((uint32_t)(q >> 32));
+        }
+    }
+}
+
 template <int ODT>
 __device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const float* acc) {
     if (ODT == RDG_BF16) {
@@ -58,11 +85,20 @@ __device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const 
 }
 
 // Lane 0 waits for a counter; returns false on timeout.
+// Lane 0 waits for a counter; returns false on timeout.  The polls are
+// relaxed device-scope loads (they read L2, where the producer's release
+// lands, without invalidating this CU's L1 on every poll -- which would slow
+// the GEMM waves sharing the CU); the caller issues one acquire fence once
+// every counter it needs is complete.  Exponential back-off (64 cycles up to
+// about 8k) keeps the polling traffic on the counters' few L2 lines low.
 __device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_ticks) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= threshold) return true;
     const uint64_t t0 = wall_clock64();
-    while (__hip_atomic_load(c, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) < threshold) {
+    int backoff = 1;
+    while (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < threshold) {
         if (wall_clock64() - t0 > timeout_ticks) return false;
-        __builtin_amdgcn_s_sleep(8);  // ~500 cycles: keeps the polling traffic on the counters' L2 lines low
+        for (int i = 0; i < backoff; ++i) __builtin_amdgcn_s_sleep(1);
+        backoff = backoff < 128 ? backoff * 2 : 128;
     }
     return true;
 }
@@ -80,12 +116,11 @@ __device__ __forceinline__ int wave_max_i32(int v) {
 // visited in index order.
 // Token t's slots into this wave's LDS row: positions (-1: no row, or a row
 // whose tile never completed) and weights.  Polling form: lane 0 first waits
-// for the counter of every row tile the token reads, then one acquire makes
-// the rows' values visible.
+// for the counter of every row tile the token reads.
 __device__ __forceinline__ void token_slots(const int32_t* __restrict__ pos, const float* __restrict__ w, int t,
                                             int K, const int32_t* signals, int rows_per_sig, int threshold,
                                             uint64_t timeout_ticks, int32_t* status, int* pos_l, float* w_l,
-                                            int lane) {
+                                            int lane, int& known_tile) {
     int p = -1;
     float wt = 0.0f;
     if (lane < K) {
@@ -96,15 +131,20 @@ __device__ __forceinline__ void token_slots(const int32_t* __restrict__ pos, con
         for (int k = 0; k < K; ++k) {
             const int pk = __shfl(p, k);
             if (pk < 0) continue;
+            const int tile = pk / rows_per_sig;
+            if (tile == known_tile) continue;  // confirmed complete for an earlier token
             int ok = 1;
             if (lane == 0) {
-                ok = wait_counter(signals + pk / rows_per_sig, threshold, timeout_ticks) ? 1 : 0;
-                if (!ok) set_status(status, RDG_ETIMEOUT, pk / rows_per_sig);
+                ok = wait_counter(signals + tile, threshold, timeout_ticks) ? 1 : 0;
+                if (!ok) set_status(status, RDG_ETIMEOUT, tile);
             }
             ok = __shfl(ok, 0);
-            if (!ok && lane == k) p = -1;  // skip the incomplete row
+            if (ok) known_tile = tile;
+            else if (lane == k) p = -1;  // skip the incomplete row
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // the rows are then read with device-scope loads (load8_published);
+        // this fence only keeps those loads after the polls
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
     // the feature loop may leave lanes idle: it reads the slots from LDS
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -145,6 +185,51 @@ __device__ __forceinline__ void combine_slice(const void* __restrict__ y, const 
     store8<ODT>(out, (size_t)t, H, v, acc);
 }
 
+// All slices of token t from published rows, G slices at a time with every
+// row load of a group issued before any is used (the device-scope loads go
+// to memory; one at a time would leave the wave waiting on each).
+template <int YDT, int ODT>
+__device__ __forceinline__ void combine_token_published(const void* __restrict__ y, const void* __restrict__ shared_out,
+                                                        void* __restrict__ out, int t, int K, int H, const int* pos_l,
+                                                        const float* w_l, int lane) {
+    constexpr int G = 7;
+    const int nvec = H / 8;
+    for (int v0 = lane; v0 < nvec; v0 += G * kWave) {
+        float acc[G][8];
+#pragma unroll
+        for (int j = 0; j < G; ++j)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int pk = pos_l[k];
+            const float wk = w_l[k];
+            if (pk < 0) continue;
+            float yv[G][8];
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                const int v = v0 + j * kWave;
+                if (v < nvec) load8_published<YDT>(y, (size_t)pk, H, v, yv[j]);
+            }
+#pragma unroll
+            for (int j = 0; j < G; ++j)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] += wk * yv[j][i];
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int v = v0 + j * kWave;
+            if (v >= nvec) continue;
+            if (shared_out != nullptr) {
+                float sv[8];
+                load8<ODT>(shared_out, (size_t)t, H, v, sv);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[j][i] += sv[i];
+            }
+            store8<ODT>(out, (size_t)t, H, v, acc[j]);
+        }
+    }
+}
+
 // Plain form: one wave per (token, 512-feature slice) unit, tokens in index
 // order.  Polling form (READY): one wave per token, visited in the order its
 // rows become ready -- token t at its last layout row max_k pos[t,k], walking
@@ -167,30 +252,54 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
         const int64_t n_units = (int64_t)T * n_slices;
         for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += stride) {
             const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
+            int none = -1;
             token_slots(pos, w, t, K, nullptr, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv],
-                        w_lds[wv], lane);
+                        w_lds[wv], lane, none);
             combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
         }
         return;
     }
-    const int64_t n_units = (int64_t)m_cap + T;
-    for (int64_t u0 = (int64_t)blockIdx.x * 4 + wv; u0 < n_units; u0 += stride) {
-        int t;
-        if (u0 < m_cap) {
-            const int src = row_src[u0];  // wave-uniform
-            if (src < 0) continue;        // padding row
-            t = src / K;
-            const int last = wave_max_i32(lane < K ? pos[(size_t)t * K + lane] : -1);
-            if (last != (int)u0) continue;  // the token is combined at its last row
-        } else {
-            t = (int)(u0 - m_cap);
-            const int last = wave_max_i32(lane < K ? pos[(size_t)t * K + lane] : -1);
-            if (last >= 0) continue;  // combined at its last row above
+    // units of RC consecutive layout rows (then of RC tokens without a row
+    // here): the tokens completed by neighbouring rows mostly share a row
+    // tile, so one confirmed poll serves them all
+    constexpr int RC = 16;
+    const int64_t row_units = ((int64_t)m_cap + RC - 1) / RC;
+    const int64_t n_units = row_units + ((int64_t)T + RC - 1) / RC;
+    int known_tile = -1;
+    for (int64_t u = (int64_t)blockIdx.x * 4 + wv; u < n_units; u += stride) {
+        // lane i < RC looks at row u*RC+i (or token (u-row_units)*RC+i): its
+        // token, and whether this unit is where that token gets combined
+        int tok = -1;
+        bool mine = false;
+        if (lane < RC) {
+            if (u < row_units) {
+                const int64_t r = u * RC + lane;
+                const int src = r < m_cap ? row_src[r] : -1;
+                if (src >= 0) {
+                    tok = src / K;
+                    int last = -1;
+                    for (int k = 0; k < K; ++k) last = max(last, pos[(size_t)tok * K + k]);
+                    mine = last == (int)r;  // the token is combined at its last row
+                }
+            } else {
+                const int64_t tt = (u - row_units) * RC + lane;
+                if (tt < T) {
+                    tok = (int)tt;
+                    int last = -1;
+                    for (int k = 0; k < K; ++k) last = max(last, pos[(size_t)tok * K + k]);
+                    mine = last < 0;  // no row here: combined in this second pass
+                }
+            }
         }
-        token_slots(pos, w, t, K, signals, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv], w_lds[wv],
-                    lane);
-        for (int slice = 0; slice < n_slices; ++slice)
-            combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
+        uint64_t todo = __ballot(mine);
+        while (todo) {
+            const int i = __builtin_ctzll(todo);
+            todo &= todo - 1;
+            const int t = __shfl(tok, i);
+            token_slots(pos, w, t, K, signals, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv],
+                        w_lds[wv], lane, known_tile);
+            combine_token_published<YDT, ODT>(y, shared_out, out, t, K, H, pos_lds[wv], w_lds[wv], lane);
+        }
     }
 }
 
@@ -202,9 +311,21 @@ hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int
                           int max_blocks, int32_t* status, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const bool ready = signals != nullptr;
-    const int64_t units = ready ? (int64_t)m_cap + T : (int64_t)T * ((H / 8 + kWave - 1) / kWave);
+    const int64_t units = ready ? ((int64_t)m_cap + 15) / 16 + ((int64_t)T + 15) / 16
+                                : (int64_t)T * ((H / 8 + kWave - 1) / kWave);
     int64_t blocks = (units + 3) / 4;
     if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+    if (ready) {
+        // Polling workgroups hold their CU resources while they wait.  A
+        // producer workgroup of the down GEMM needs most of a CU, so polling
+        // workgroups spread over every CU could leave it nowhere to run until
+        // the waits time out: at most a quarter of the CUs' worth of them.
+        int dev = 0, n_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return hipErrorInvalidDevice;
+        const int64_t cap = n_cu / 4 > 0 ? n_cu / 4 : 1;
+        if (blocks > cap) blocks = cap;
+    }
 #define RDG_COMBINE(YD, OD)                                                                                    \
     do {                                                                                                       \
         if (ready)                                                                                             \

@@ -154,6 +154,7 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
     const int f0 = (SIGNAL ? blockIdx.x : blockIdx.y) * 128;
+    if (f0 >= a.Nout) return;  // signalled grids are padded to a multiple of 8 column blocks (uniform)
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int fw = f0 + wv * 32;
     const size_t wstride = (size_t)a.Kdim * ESZ;
@@ -318,14 +319,7 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
         }
     }
 
-    if (SIGNAL) {
-        // every thread's stores are complete and visible device-wide before
-        // the workgroup's single release-ordered increment of the tile counter
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / BT, 128, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (SIGNAL) signal_done(a.signals + row0 / BT, 128);
 }
 
 
@@ -372,6 +366,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
     const int f0 = (SIGNAL ? blockIdx.x : blockIdx.y) * (16 * FPW);
+    if (f0 >= a.Nout) return;  // signalled grids are padded to a multiple of 8 column blocks (uniform)
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const size_t wstride = (size_t)a.Kdim * ESZ;
 
@@ -499,12 +494,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
             }
         }
     }
-    if (SIGNAL) {
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / BT, 16 * FPW, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (SIGNAL) signal_done(a.signals + row0 / BT, 16 * FPW);
 }
 
 
@@ -571,7 +561,7 @@ hipError_t launch_skinny(const FfnCall& c, hipStream_t s) {
     if (c.stages & 2) {
         const KArgs d = down_args(c);
         if (c.signals)
-            k_ffn_skinny<DT, false, true, 2, NR><<<dim3(c.H / 32, c.n_tiles_max), block, 0, s>>>(d);
+            k_ffn_skinny<DT, false, true, 2, NR><<<dim3(round8(c.H / 32), c.n_tiles_max), block, 0, s>>>(d);
         else
             k_ffn_skinny<DT, false, false, 2, NR><<<dim3(c.n_tiles_max, c.H / 32), block, 0, s>>>(d);
     }
@@ -590,7 +580,7 @@ hipError_t launch_bt(const FfnCall& c, hipStream_t s) {
     if (c.stages & 2) {
         const KArgs d = down_args(c);
         if (c.signals)
-            k_ffn<DT, BT, false, true><<<dim3(c.H / 128, c.n_tiles_max), block, 0, s>>>(d);
+            k_ffn<DT, BT, false, true><<<dim3(round8(c.H / 128), c.n_tiles_max), block, 0, s>>>(d);
         else
             k_ffn<DT, BT, false, false><<<dim3(c.n_tiles_max, c.H / 128), block, 0, s>>>(d);
     }

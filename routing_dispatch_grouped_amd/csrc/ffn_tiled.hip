@@ -16,7 +16,7 @@
 // all 128 token rows (eight 16-row MFMA tiles), so each token operand read
 // from LDS feeds two MFMAs and each weight operand eight.
 //
-// The reduction dimension is walked in chunks of 256 bytes per row.  The
+// The reduction dimension is walked in chunks of CB bytes per row.  The
 // token tile is shared by the eight waves, so its chunks go through a
 // two-slot LDS ring filled by direct global->LDS loads; the slot of 16-byte
 // piece c of row r is c ^ (r % 16) (chosen through each lane's source
@@ -49,9 +49,6 @@ typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
 constexpr int NW = 8;                 // waves per workgroup
 constexpr int TB = 128;               // rows per tile
-constexpr int CB = 256;               // bytes of each row per chunk
-constexpr int CHUNK_LDS = TB * CB;    // token bytes per chunk
-constexpr int XLOADS = CHUNK_LDS / 1024 / NW;  // KiB loads per wave and chunk
 constexpr int NCT = TB / 16;          // 16-row token tiles per wave
 constexpr int NRT = 2;                // 16-row weight tiles per wave
 constexpr int PANEL = NW * NRT * 16;  // weight rows per workgroup
@@ -59,10 +56,16 @@ constexpr int PANEL = NW * NRT * 16;  // weight rows per workgroup
 template <int DT>
 struct TOp;
 
+// Per type: the chunk CB (bytes of each row per chunk: two chunks of token
+// rows and of weights in flight must fit the register budget of two waves per
+// SIMD), the MFMA step KS (reduction elements), element size, the packed
+// weight tile size BLK (see pack.hip), MFMA steps per chunk, and the weight
+// load instructions per chunk.
 template <>
 struct TOp<RDG_BF16> {
     using op_t = bf16x8_t;
-    static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);  // 4 MFMA steps per chunk
+    static constexpr int CB = 512;
+    static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);
     static constexpr int WLOADS = NRT * STEPS;                                   // load instructions
     __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
@@ -84,7 +87,8 @@ struct TOp<RDG_BF16> {
 template <>
 struct TOp<RDG_FP8_E4M3> {
     using op_t = i32x8_t;
-    static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // 2 MFMA steps (scale blocks) per chunk
+    static constexpr int CB = 256;
+    static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // steps = 1x128 scale blocks
     static constexpr int WLOADS = NRT * STEPS * 2;
     __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
@@ -154,32 +158,37 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 struct Ring {
-    uint8_t* x;  // CHUNK_LDS bytes: the token chunk
-    float* s;    // fp8: [128 rows][2 blocks] activation scales of the chunk
+    uint8_t* x;  // 128 * CB bytes: the token chunk
+    float* s;    // fp8: [128 rows][SPB blocks] activation scales of the chunk
 };
 
-// Request chunk kc of the tile's token rows: XLOADS direct KiB loads per wave
+// Request chunk kc of the tile's token rows: 16 * CB / 1024 direct KiB loads per wave
 // (rows past the tile's valid rows re-read the last valid row: in bounds,
 // never stored); fp8: one load of 32 activation scales per wave.
 template <int DT>
 __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, int row0, int nvalid, int kc,
                                             const Ring& ring, int wv, int lane) {
+    constexpr int CB = TOp<DT>::CB, XLOADS = TB * CB / 1024 / NW, SPB = CB / 128;
+    static_assert(SPB * 16 <= 64 && 1024 % CB == 0, "chunk shape");
+    constexpr int PPR = CB / 16;          // 16-byte pieces per row
 #pragma unroll
     for (int i = 0; i < XLOADS; ++i) {
-        const int q = wv * XLOADS + i;     // LDS bytes [q*1024, q*1024+1024)
-        const int r = q * 4 + lane / 16;   // tile row of this lane's 16 bytes
-        const int slot = lane % 16;
-        const int c = slot ^ (r & 15);     // source piece for this slot
+        const int q = wv * XLOADS + i;             // LDS bytes [q*1024, q*1024+1024)
+        const int r = q * (1024 / CB) + lane / PPR;  // tile row of this lane's 16 bytes
+        const int slot = lane % PPR;
+        const int c = slot ^ (r & 15);             // source piece for this slot
         const int rr = r < nvalid ? r : nvalid - 1;
         const uint8_t* src = a.X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.x + q * 1024), 16, 0, 0);
     }
     if (DT == RDG_FP8_E4M3) {
-        // lanes 0..31 of wave w: rows 16w + l/2, scale block 2kc + l%2
-        const int r = wv * 16 + (lane & 31) / 2;
+        // lanes 0..16*SPB-1 of wave w: row 16w + l/SPB, scale block SPB*kc + l%SPB
+        const int l = lane % (16 * SPB);
+        const int r = wv * 16 + l / SPB;
         const int rr = r < nvalid ? r : nvalid - 1;
-        const float* src = a.Xs + (size_t)(row0 + rr) * nkb + 2 * kc + (lane & 1);
-        if (lane < 32) __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.s + wv * 32), 4, 0, 0);
+        const float* src = a.Xs + (size_t)(row0 + rr) * nkb + SPB * kc + l % SPB;
+        if (lane < 16 * SPB)
+            __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.s + wv * 16 * SPB), 4, 0, 0);
     }
 }
 
@@ -189,19 +198,22 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     using op_t = typename O::op_t;
     constexpr int S = O::STEPS;
     constexpr bool FP8 = DT == RDG_FP8_E4M3;
+    constexpr int CB = O::CB, CHUNK_LDS = TB * CB, SPB = CB / 128;
     __shared__ __attribute__((aligned(16))) uint8_t lx0[CHUNK_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t lx1[CHUNK_LDS];
-    __shared__ __attribute__((aligned(16))) float ls0[FP8 ? TB * 2 : 4];
-    __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * 2 : 4];
+    __shared__ __attribute__((aligned(16))) float ls0[FP8 ? TB * SPB : 4];
+    __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * SPB : 4];
     const Ring ring[2] = {{lx0, ls0}, {lx1, ls1}};
 
     int fb, tile;
     if (SIGNAL) {
-        // tile-major in dispatch order (grid x = column panel): row tiles
-        // complete in layout order for the polling consumer; XCD x then runs
-        // the panels fb = x (mod 8) of every tile and keeps them in its L2
+        // tile-major in dispatch order (grid x = column panel, padded to a
+        // multiple of 8): row tiles complete in layout order for the polling
+        // consumer, and XCD x runs the panels fb = x (mod 8) of every tile and
+        // keeps them in its L2
         fb = blockIdx.x;
         tile = blockIdx.y;
+        if (fb * PANEL >= a.Nout) return;  // padding workgroup (uniform)
     } else {
         // XCD-aware renumbering: hardware block b runs on XCD b % 8, which
         // gets ceil((total - x) / 8) blocks; give XCD x the contiguous logical
@@ -266,41 +278,45 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             for (int s = 0; s < S; ++s) swr[s] = wsc[kc * S + s];
         }
     };
+    // One chunk: items i = (step s, token tile ct) in order.  The token
+    // operand of item i+2 is read from LDS while item i's MFMAs run (a
+    // three-deep register ring), and fp8 promotes item i-1's block partials
+    // behind item i's MFMAs; the scheduling barrier after each item keeps the
+    // compiler from hoisting a chunk's worth of LDS reads (registers).
     auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT], const float (&swr)[S]) {
+        constexpr int NI = S * NCT;
+        op_t xb[3];
+        float fb[4];
+        f32x4_t p[2][NRT];
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        auto fetch = [&](int i) {
+            const int si = i / NCT, r = (i % NCT) * 16 + (lane & 15);
+            xb[i % 3] = O::load_x(rg.x, r, si, lane >> 4);
+            if (FP8) fb[i % 4] = rg.s[r * SPB + si] * swr[si];
+        };
+        fetch(0);
+        fetch(1);
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            // one step's token operands at a time (the scheduler would
-            // otherwise hoist a whole chunk's LDS reads and run out of registers)
-            __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < NI; ++i) {
+            const int si = i / NCT, ct = i % NCT;
+            if (i + 2 < NI) fetch(i + 2);
             if (!FP8) {
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const op_t xo = O::load_x(rg.x, ct * 16 + (lane & 15), s, lane >> 4);
-#pragma unroll
-                    for (int rt = 0; rt < NRT; ++rt) acc[rt][ct] = O::mma(acc[rt][ct], wr[s][rt], xo);
-                }
+                for (int rt = 0; rt < NRT; ++rt) acc[rt][ct] = O::mma(acc[rt][ct], wr[si][rt], xb[i % 3]);
             } else {
-                // the block partials of token tile ct are promoted while the
-                // MFMAs of tile ct+1 run (two partial sets live at a time)
-                f32x4_t p[2][NRT];
-                float f[2];
-                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ct = 0; ct <= NCT; ++ct) {
-                    if (ct < NCT) {
-                        const int r = ct * 16 + (lane & 15);
-                        const op_t xo = O::load_x(rg.x, r, s, lane >> 4);
-                        f[ct % 2] = rg.s[r * 2 + s] * swr[s];
+                for (int rt = 0; rt < NRT; ++rt) p[i % 2][rt] = O::mma(z, wr[si][rt], xb[i % 3]);
+                if (i > 0) {
+                    const int cp = (i - 1) % NCT;
 #pragma unroll
-                        for (int rt = 0; rt < NRT; ++rt) p[ct % 2][rt] = O::mma(z, wr[s][rt], xo);
-                    }
-                    if (ct > 0) {
-#pragma unroll
-                        for (int rt = 0; rt < NRT; ++rt) acc[rt][ct - 1] += p[(ct - 1) % 2][rt] * f[(ct - 1) % 2];
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
+                    for (int rt = 0; rt < NRT; ++rt) acc[rt][cp] += p[(i - 1) % 2][rt] * fb[(i - 1) % 4];
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (FP8) {
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[rt][NCT - 1] += p[(NI - 1) % 2][rt] * fb[(NI - 1) % 4];
         }
     };
 
@@ -415,12 +431,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             }
         }
     }
-    if (SIGNAL) {
-        __threadfence();
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(a.signals + row0 / TB, PANEL, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (SIGNAL) signal_done(a.signals + row0 / TB, PANEL);
 }
 
 template <int DT>
@@ -439,7 +450,7 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
                 static_cast<const uint8_t*>(c.h), c.h_s, static_cast<const uint8_t*>(c.W2), nullptr, c.W2_s,
                 nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
         if (c.signals)
-            k_ffn_tiled<DT, false, true><<<dim3(c.H / PANEL, c.n_tiles_max), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, true><<<dim3(round8(c.H / PANEL), c.n_tiles_max), block, 0, s>>>(d);
         else
             k_ffn_tiled<DT, false, false><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
     }
@@ -450,11 +461,12 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
 
 // bf16 / fp8 with I a multiple of 128 (the gate/up feature panel) and H a
 // multiple of 256 (the down column panel); both reduction dimensions in whole
-// 256-byte chunks.
+// chunks (512 bytes bf16, 256 bytes fp8).
 bool tiled_supported(int dtype, int H, int I) {
     const int esz = dtype == RDG_BF16 ? 2 : dtype == RDG_FP8_E4M3 ? 1 : 0;
-    return esz > 0 && I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * esz) % CB == 0 &&
-           ((int64_t)I * esz) % CB == 0;
+    const int cb = dtype == RDG_BF16 ? TOp<RDG_BF16>::CB : TOp<RDG_FP8_E4M3>::CB;
+    return esz > 0 && I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * esz) % cb == 0 &&
+           ((int64_t)I * esz) % cb == 0;
 }
 
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s) {

@@ -119,6 +119,27 @@ hipError_t launch_pack(const void* W, int dtype, int n_mat, int rows, int cols, 
 hipError_t launch_quantize(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
                            float* scales, hipStream_t s);
 
+// End of a signalled down-GEMM workgroup: publish `cols` finished output
+// columns of its row tile.  Every wave first waits for its own stores (they
+// are then in this XCD's L2); after the barrier one wave releases at device
+// scope -- on this part a write-back of the XCD's L2 to memory, where other
+// XCDs' device-scope loads read -- and adds to the counter.  Deliberately no
+// __threadfence(): its acquire half also invalidates the XCD's L2, throwing
+// away the weight panels the other workgroups on that XCD are re-reading.
+__device__ __forceinline__ void signal_done(int32_t* counter, int cols) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(counter, cols, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// Column blocks of a signalled (tile-major) down GEMM grid, padded to a
+// multiple of the 8 XCDs so that a column block always runs on the same XCD
+// (hardware workgroup b runs on XCD b % 8) and its weights stay in that L2.
+inline unsigned round8(int n) { return (unsigned)((n + 7) / 8 * 8); }
+
 struct FfnCall {
     const int32_t* offsets;
     const int32_t* masked_m;

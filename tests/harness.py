@@ -137,6 +137,12 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
         thr = m.rdg_signal_threshold(H, dt)
     out_dt = m.RDG_F32 if dt == m.RDG_F32 else m.RDG_BF16
     out = torch.empty((T, H), dtype=ydt, device=x.device)
+    if signals:
+        # NaN in y and out before a signalled run: a combine that read a row
+        # before its tile was published, or skipped a token, cannot pass as a
+        # left-over of an earlier identical run
+        m.rdg_fill_i32(y.view(torch.int32), -1)
+        m.rdg_fill_i32(out.view(torch.int32), -1)
     y_dt = m.RDG_F32 if dt == m.RDG_F32 else m.RDG_BF16
     if concurrent:
         s_gemm = torch.cuda.current_stream()
