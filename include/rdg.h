@@ -134,7 +134,8 @@ size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);
  * layout is deterministic.  Overflow drops the extra rows and sets status
  * RDG_ECAPACITY (masked: detail = the largest count; contiguous: detail =
  * the rows needed).  Padding rows of x_perm are left untouched.
- * H must be a multiple of 16 (fp8: of 128).  T = 0 is allowed. */
+ * H must be a multiple of 16 (fp8: of 128).  T = 0 is allowed (the layout
+ * is cleared; x, ids, x_perm and the scale pointers may then be NULL). */
 int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
                  const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream);
 
@@ -167,7 +168,8 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  *             ordering at device scope; a tile is complete when its counter
  *             reaches rdg_signal_threshold(H, dtype) = H.
  * Rows outside [offsets[e], offsets[e] + masked_m[e]) are neither read nor
- * written.  H and I must be multiples of 128. */
+ * written.  H and I must be multiples of 128.  A layout with L->n_rows = 0
+ * is a no-op (nothing is launched; the buffer pointers may be NULL). */
 int rdg_grouped_ffn(const rdg_layout* L, int dtype, int H, int I, const void* x_perm, const float* x_perm_scales,
                     const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
                     const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,

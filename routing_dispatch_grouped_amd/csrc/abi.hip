@@ -121,7 +121,8 @@ int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, 
         case RDG_BF16: esz = 2; break;
         case RDG_FP8_E4M3:
             esz = 1;
-            if (H % 128 != 0 || !x_scales || !x_perm_scales) return RDG_EINVAL;
+            if (H % 128 != 0) return RDG_EINVAL;
+            if (T > 0 && (!x_scales || !x_perm_scales)) return RDG_EINVAL;
             break;
         default: return RDG_EINVAL;
     }
@@ -153,6 +154,7 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
                             void* y, int32_t* signals, int stages, rdg_stream_t stream) {
     if (!layout_ok(L) || H < 128 || H % 128 != 0 || I < 128 || I % 128 != 0) return RDG_EINVAL;
     if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3) return RDG_EINVAL;
+    if (L->n_rows == 0) return RDG_OK;  // nothing dispatched: no rows, nothing to launch
     const bool fp8 = dtype == RDG_FP8_E4M3;
     if (!h_ws || !aligned16(h_ws) || (fp8 && !h_scales_ws)) return RDG_EINVAL;
     if (stages & 1) {

@@ -1,0 +1,112 @@
+"""GPU edge cases of the whole path against the oracle: an empty layer,
+masked-capacity drops carried through the FFN and the combine, one expert
+holding every token in whole 128-row tiles (no padding), and hidden sizes
+that are multiples of 128 but not of 256 (the 128-row tiled kernels decline
+them and the 64-row kernels take over)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from harness import (DEV, ExpertSet, check_rows, dt_code, np_of, out_as_f64, quantize_act, rdg, run_routed,
+                     tolerance)
+
+pytestmark = pytest.mark.gpu
+
+
+def _cfg(dtype, H=512, I=256, N=8, K=2, wid=700):
+    return dict(wid=wid, H=H, N=N, n_group=1, topk_group=1, K=K, I=I, shared_I=0, dtype=dtype, scale=1.0,
+                logits="normal", name="edge_" + dtype)
+
+
+def _inputs(cfg, T):
+    x = synth.x(cfg, T, device=DEV)
+    x_s, xo, xo_s = None, np_of(x), None
+    if cfg["dtype"] == "fp8":
+        x, x_s = quantize_act(x)
+        if T:
+            xo, xo_s = oracle.quantize_fp8(xo, 1)
+    return x, x_s, xo, xo_s
+
+
+def _compare(cfg, got, ref, what):
+    err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
+    check_rows(got, ref, cfg, what)
+    print("%s rel_err=%.3e" % (what, err), flush=True)
+    assert err <= tolerance(cfg), err
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kind", [0, 1])
+def test_empty_layer(dtype, kind):
+    m = rdg()
+    cfg = _cfg(dtype)
+    x, x_s, _, _ = _inputs(cfg, 0)
+    ids = torch.zeros((0, cfg["K"]), dtype=torch.int32, device=DEV)
+    w = torch.zeros((0, cfg["K"]), dtype=torch.float32, device=DEV)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, ids, w, experts, kind, block_m=128, m_max=128 if kind else 0)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    assert r["out"].shape == (0, cfg["H"])
+    assert int(np_of(r["L"].counts).sum()) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+def test_masked_capacity_drop_through_the_layer(dtype):
+    """Rows past m_max are dropped (status RDG_ECAPACITY, detail = largest
+    count); the output is the sum over the kept rows only."""
+    m = rdg()
+    cfg = _cfg(dtype, N=4, K=2, wid=710)
+    T, m_max = 96, 16
+    rng = np.random.default_rng(3)
+    ids_np = np.stack([rng.choice(cfg["N"], size=2, replace=False) for _ in range(T)]).astype(np.int32)
+    w_np = rng.uniform(0.2, 0.8, size=(T, 2)).astype(np.float32)
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), experts,
+                   m.RDG_MASKED, m_max=m_max)
+    lay = oracle.layout(ids_np, cfg["N"], oracle.MASKED, m_max=m_max)
+    assert m.rdg_check_status(r["L"]) == (lay["status"], lay["detail"]) == (m.RDG_ECAPACITY,
+                                                                              int(np.bincount(ids_np.ravel()).max()))
+    kept = np.where(lay["pos"].reshape(T, 2) >= 0, ids_np, -1).astype(np.int32)
+    assert (kept < 0).sum() > 0
+    ref = oracle.moe_layer(dt_code(cfg), xo, kept, w_np, [experts.oracle_expert(j) for j in range(cfg["N"])],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "capacity drop %s" % dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("T", [128, 256, 129])
+def test_one_expert_whole_tiles(dtype, T):
+    """Every token to expert 2 of 4 with K = 1: exactly T/128 full tiles (T=129: one row past them)."""
+    m = rdg()
+    cfg = _cfg(dtype, N=4, K=1, wid=720 + T)
+    ids_np = np.full((T, 1), 2, np.int32)
+    w_np = np.full((T, 1), 0.75, np.float32)
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), experts,
+                   m.RDG_CONTIGUOUS, block_m=128)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    assert np_of(r["L"].counts).tolist() == [0, 0, T, 0]
+    ref = oracle.moe_layer(dt_code(cfg), xo, ids_np, w_np, [None, None, experts.oracle_expert(2), None],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "one expert %s T=%d" % (dtype, T))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_hidden_not_a_multiple_of_256(dtype):
+    m = rdg()
+    cfg = dict(_cfg(dtype, H=384, I=384, N=4, K=2, wid=730), n_group=2, topk_group=1)
+    T = 600
+    logits = synth.logits(cfg, T)
+    ri, rw = oracle.route(logits, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ri).to(DEV), torch.from_numpy(rw).to(DEV), experts,
+                   m.RDG_CONTIGUOUS, block_m=128)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    ref = oracle.moe_layer(dt_code(cfg), xo, ri, rw, [experts.oracle_expert(j) for j in range(cfg["N"])],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "H=384 %s" % dtype)
