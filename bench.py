@@ -315,6 +315,10 @@ def main():
     masked_m = b.L.masked_m.cpu().numpy()
     active = int((masked_m > 0).sum())
     rows = int(masked_m.sum())
+    counts = b.L.counts.cpu().numpy()
+    # load balance of the local experts, mean / max of their routed rows (the
+    # statistic expert-load rebalancing raises)
+    balance = float(counts.mean() / counts.max()) if counts.max() > 0 else 1.0
 
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -354,7 +358,8 @@ def main():
         value = b.T / (ms * 1e-3)
     conf = {"workload": args.workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
-            "layout": cfg["layout"], "active_experts": active, "routed_rows": rows}
+            "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
+            "load_balance_mean_over_max": round(balance, 4)}
     if "m_max" in cfg:
         conf["m_max"] = cfg["m_max"]
     if b.rank:

@@ -77,6 +77,13 @@ enum { RDG_CONTIGUOUS = 0, RDG_MASKED = 1 };            /* layout kinds */
  *   row_src   [m_cap]     entry t*K+k stored in each row, or -1 (padding)
  *   status    [2]         {code, detail}; cleared by rdg_dispatch
  *   work      rdg_dispatch_workspace_bytes(T, K, n_local) bytes
+ *   expert_load  NULL, or [n_local] int64 kept by the caller across calls:
+ *             rdg_dispatch adds each expert's routed-row count (before any
+ *             capacity drop) to it -- the expert-load statistics that
+ *             rebalancing works from ([LEP] "EPLB": replicas and placement
+ *             follow the recorded load; [H100] "Case study: expert
+ *             distribution statistics").  The caller zeroes it; concurrent
+ *             dispatches may share it (device-scope atomic adds).
  */
 typedef struct rdg_layout {
     int32_t kind, n_local, block_m, m_max, m_cap, n_rows;
@@ -87,6 +94,7 @@ typedef struct rdg_layout {
     int32_t* row_src;
     int32_t* status;
     void* work;
+    int64_t* expert_load;
 } rdg_layout;
 
 /* Group-limited top-k gating ([DEEP] "group-limited gating": pick the best

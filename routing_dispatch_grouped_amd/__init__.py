@@ -27,7 +27,7 @@ class rdg_layout(ctypes.Structure):
                 ("m_max", ctypes.c_int32), ("m_cap", ctypes.c_int32), ("n_rows", ctypes.c_int32),
                 ("counts", ctypes.c_void_p), ("offsets", ctypes.c_void_p), ("masked_m", ctypes.c_void_p),
                 ("pos", ctypes.c_void_p), ("row_src", ctypes.c_void_p), ("status", ctypes.c_void_p),
-                ("work", ctypes.c_void_p)]
+                ("work", ctypes.c_void_p), ("expert_load", ctypes.c_void_p)]
 
 
 if not os.path.exists(LIB_PATH):
@@ -87,7 +87,7 @@ def _check(rc, what):
 class Layout:
     """Device buffers of an rdg_layout, allocated with torch on ``device``."""
 
-    def __init__(self, kind, n_local, T, K, device, block_m=128, m_max=0, m_cap=None):
+    def __init__(self, kind, n_local, T, K, device, block_m=128, m_max=0, m_cap=None, expert_load=None):
         import torch
         self.kind, self.n_local, self.T, self.K = kind, n_local, T, K
         n_rows = T * K
@@ -105,7 +105,8 @@ class Layout:
         self.c = rdg_layout(kind, n_local, block_m, m_max, m_cap, n_rows,
                             self.counts.data_ptr(), self.offsets.data_ptr(), self.masked_m.data_ptr(),
                             self.pos.data_ptr(), self.row_src.data_ptr(), self.status.data_ptr(),
-                            self.work.data_ptr())
+                            self.work.data_ptr(), expert_load.data_ptr() if expert_load is not None else None)
+        self.expert_load = expert_load  # optional int64 [n_local] accumulated by rdg_dispatch
         self.m_cap = m_cap
         self.block_m = block_m
         self.m_max = m_max

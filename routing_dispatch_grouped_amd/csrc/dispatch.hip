@@ -147,7 +147,7 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
                                                int kind, int block_m, int m_max, int m_cap,
                                                int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
                                                int32_t* __restrict__ masked_m, int32_t* __restrict__ tile_off,
-                                               int32_t* __restrict__ status) {
+                                               int32_t* __restrict__ status, int64_t* __restrict__ expert_load) {
     __shared__ int lds[32];
     const int e = threadIdx.x;
     const bool act = e < n_local;
@@ -171,6 +171,9 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
             run += v;
         }
         counts[e] = run;
+        // the expert-load recorder: routed rows before any capacity drop
+        if (expert_load != nullptr)
+            atomicAdd(reinterpret_cast<unsigned long long*>(expert_load + e), (unsigned long long)run);
     }
     int seg = 0;
     if (act) seg = kind == RDG_MASKED ? m_max : (run + block_m - 1) / block_m * block_m;
@@ -319,7 +322,7 @@ hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, 
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     k_scan<<<1, 1024, 0, s>>>(chunk_counts, n_chunks, L.n_local, L.kind, L.block_m, L.m_max, L.m_cap, L.counts,
-                              L.offsets, L.masked_m, tile_off, L.status);
+                              L.offsets, L.masked_m, tile_off, L.status, L.expert_load);
     err = hipGetLastError();
     if (err != hipSuccess || T == 0) return err;
     const int n_scales = x_scales ? H / 128 : 0;

@@ -52,8 +52,9 @@ def test_host_queries_and_validation():
 
 def test_layout_struct_matches_header():
     import routing_dispatch_grouped_amd as rdg
-    # 6 int32 fields then 7 pointers
-    assert ctypes.sizeof(rdg.rdg_layout) == 6 * 4 + 7 * 8
+    # 6 int32 fields then 8 pointers
+    assert ctypes.sizeof(rdg.rdg_layout) == 6 * 4 + 8 * 8
+    assert rdg.rdg_layout.expert_load.offset == 24 + 7 * 8
     assert rdg.rdg_layout.counts.offset == 24
 
 

@@ -137,3 +137,27 @@ def test_quantiser_bit_exact(rows, cols, block_rows, src):
     rq, rs = oracle.quantize_fp8(host, block_rows)
     assert np.array_equal(np_of(s), rs)
     assert np.array_equal(np_of(q), rq)
+
+
+def test_expert_load_recorder():
+    """rdg_dispatch accumulates each expert's routed rows (before capacity
+    drops) into the layout's expert_load buffer across calls."""
+    m = rdg()
+    E, K = 24, 6
+    load = torch.zeros(E, dtype=torch.int64, device=DEV)
+    want = np.zeros(E, np.int64)
+    rng = np.random.default_rng(11)
+    for T, kind, m_max, holes in ((300, m.RDG_CONTIGUOUS, 0, 0.0), (200, m.RDG_MASKED, 20, 0.0),
+                                  (157, m.RDG_CONTIGUOUS, 0, 0.3), (0, m.RDG_MASKED, 8, 0.0)):
+        ids_np = _ids(rng, T, K, E, skew=True, holes=holes)
+        L = m.Layout(kind, E, T, K, DEV, block_m=64, m_max=m_max, expert_load=load)
+        x = torch.zeros((T, 128), dtype=torch.bfloat16, device=DEV)
+        xp = torch.zeros((L.m_cap, 128), dtype=torch.bfloat16, device=DEV)
+        m.rdg_dispatch(x, None, m.RDG_BF16, torch.from_numpy(ids_np).to(DEV), L, xp)
+        st = m.rdg_check_status(L)
+        ref = oracle.layout(ids_np, E, oracle.MASKED if kind == m.RDG_MASKED else oracle.CONTIGUOUS, block_m=64,
+                            m_max=m_max)
+        assert st == (ref["status"], ref["detail"])
+        want += ref["counts"]
+        assert np.array_equal(np_of(load), want)
+    assert want.sum() > 0
