@@ -10,17 +10,19 @@
 // pull request, sections 2-3).
 //
 // Design for CDNA4.  A workgroup is 8 waves (two per SIMD) and owns a tile of
-// 128 layout rows of one expert and a panel of 256 weight rows: gated, rows
-// [f0, f0+128) of W1 (waves 0-3) and of W3 (waves 4-7); down, rows [f0,
-// f0+256) of W2.  Wave w owns 32 weight rows (two 16-row MFMA tiles) against
-// all 128 token rows (eight 16-row MFMA tiles), so each token operand read
-// from LDS feeds two MFMAs and each weight operand eight.
+// 128 layout rows of one expert and a panel of weight rows.  Wave w owns NRT
+// 16-row weight tiles against all 128 token rows (eight 16-row MFMA tiles), so
+// each token operand read from LDS feeds NRT MFMAs and each weight operand
+// eight.  Gated, a wave's first NRT/2 tiles are rows of W1 and the others the
+// same rows of W3: the gate and up values of one feature meet in one lane, and
+// the SiLU-gated product needs no exchange between waves.  Down, a wave's
+// tiles are consecutive rows of W2 (output columns).
 //
 // The reduction dimension is walked in chunks of CB bytes per row.  The
 // token tile is shared by the eight waves, so its chunks go through a
-// two-slot LDS ring filled by direct global->LDS loads; the slot of 16-byte
-// piece c of row r is c ^ (r % 16) (chosen through each lane's source
-// address), which makes the MFMA-layout LDS reads conflict-free.  Weight
+// two-slot LDS ring filled by direct global->LDS loads; each 16-byte piece is
+// stored at a row-dependent XOR of its index (chosen through each lane's
+// source address) that makes the MFMA-layout LDS reads conflict-free.  Weight
 // operand tiles are private to a wave and arrive packed (pack.hip: one
 // contiguous KiB per load instruction) straight into one of two register
 // sets; a weight panel is re-read by every row tile of its expert, mostly
@@ -47,26 +49,38 @@ typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
 
-constexpr int NW = 8;                 // waves per workgroup
-constexpr int TB = 128;               // rows per tile
-constexpr int NCT = TB / 16;          // 16-row token tiles per wave
-constexpr int NRT = 2;                // 16-row weight tiles per wave
-constexpr int PANEL = NW * NRT * 16;  // weight rows per workgroup
+constexpr int NW = 8;         // waves per workgroup
+constexpr int TB = 128;       // rows per tile
+constexpr int NCT = TB / 16;  // 16-row token tiles per wave
 
 template <int DT>
 struct TOp;
 
-// Per type: the chunk CB (bytes of each row per chunk: two chunks of token
-// rows and of weights in flight must fit the register budget of two waves per
-// SIMD), the MFMA step KS (reduction elements), element size, the packed
-// weight tile size BLK (see pack.hip), MFMA steps per chunk, and the weight
-// load instructions per chunk.
+// LDS slot of 16-byte piece c of tile row r in a chunk of CB bytes per row.
+// One MFMA operand read touches one piece of 16 consecutive rows; the XOR
+// puts those 16 pieces in distinct 16-byte bank groups (rows of 256 bytes or
+// more: by r % 16; rows of 128 bytes, two to a 256-byte bank cycle: by
+// (r / 2) % 8).  An involution, so it also maps slots back to pieces.
+template <int CB>
+__device__ __forceinline__ int piece_slot(int r, int c) {
+    return CB >= 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+// Per type: NRT (16-row weight tiles per wave) and the chunk CB (bytes of
+// each row per chunk), sized so that two chunks of weights in registers, the
+// accumulators and the operand pipeline fit two waves per SIMD (bf16: 64
+// weight rows per wave, so each token operand read from LDS feeds four MFMAs;
+// fp8 keeps registers for the block partials it promotes); the MFMA step KS
+// (reduction elements), element size, the packed weight tile size BLK (see
+// pack.hip) and MFMA steps per chunk.
+template <int DT>
+struct TOp;
+
 template <>
 struct TOp<RDG_BF16> {
     using op_t = bf16x8_t;
-    static constexpr int CB = 512;
+    static constexpr int NRT = 4, CB = 128;
     static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);
-    static constexpr int WLOADS = NRT * STEPS;                                   // load instructions
     __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
@@ -76,8 +90,7 @@ struct TOp<RDG_BF16> {
     }
     // token operand of step s for local row r, lane group g: 16-byte piece 4s+g
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
-        const int c = s * 4 + g;
-        return *reinterpret_cast<const bf16x8_t*>(buf + r * CB + ((c ^ (r & 15)) << 4));
+        return *reinterpret_cast<const bf16x8_t*>(buf + r * CB + (piece_slot<CB>(r, s * 4 + g) << 4));
     }
     __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -87,9 +100,8 @@ struct TOp<RDG_BF16> {
 template <>
 struct TOp<RDG_FP8_E4M3> {
     using op_t = i32x8_t;
-    static constexpr int CB = 256;
+    static constexpr int NRT = 2, CB = 256;
     static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // steps = 1x128 scale blocks
-    static constexpr int WLOADS = NRT * STEPS * 2;
     __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
         for (int s = 0; s < STEPS; ++s)
@@ -107,8 +119,8 @@ struct TOp<RDG_FP8_E4M3> {
     // 32 bytes: pieces 8s+2g and 8s+2g+1
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
         const int c = s * 8 + g * 2;
-        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(buf + r * CB + ((c ^ (r & 15)) << 4));
-        const i32x4_t b = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (((c + 1) ^ (r & 15)) << 4));
+        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (piece_slot<CB>(r, c) << 4));
+        const i32x4_t b = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (piece_slot<CB>(r, c + 1) << 4));
         op_t o;
         o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
         o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
@@ -118,6 +130,9 @@ struct TOp<RDG_FP8_E4M3> {
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
     }
 };
+
+template <int DT>
+constexpr int panel_rows() { return NW * TOp<DT>::NRT * 16; }  // weight rows per workgroup
 
 struct TArgs {
     const int32_t* offsets;
@@ -160,29 +175,31 @@ __device__ __forceinline__ void lds_barrier() {
 struct Ring {
     uint8_t* x;  // 128 * CB bytes: the token chunk
     float* s;    // fp8: [128 rows][SPB blocks] activation scales of the chunk
+    float* w;    // fp8: [NW waves][2][STEPS] the chunk's weight block scales of each wave (W1 / W2, W3)
 };
 
-// Request chunk kc of the tile's token rows: 16 * CB / 1024 direct KiB loads per wave
-// (rows past the tile's valid rows re-read the last valid row: in bounds,
-// never stored); fp8: one load of 32 activation scales per wave.
+// Request chunk kc of the tile's token rows: 128 * CB / 1024 / NW direct KiB
+// loads per wave (rows past the tile's valid rows re-read the last valid row:
+// in bounds, never stored); fp8: one load of the chunk's activation scales of
+// 16 rows per wave.
 template <int DT>
 __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, int row0, int nvalid, int kc,
                                             const Ring& ring, int wv, int lane) {
     constexpr int CB = TOp<DT>::CB, XLOADS = TB * CB / 1024 / NW, SPB = CB / 128;
-    static_assert(SPB * 16 <= 64 && 1024 % CB == 0, "chunk shape");
-    constexpr int PPR = CB / 16;          // 16-byte pieces per row
+    constexpr int PPR = CB / 16;  // 16-byte pieces per row
+    static_assert(XLOADS >= 1 && 1024 % CB == 0 && XLOADS * NW * 1024 == TB * CB, "chunk shape");
 #pragma unroll
     for (int i = 0; i < XLOADS; ++i) {
-        const int q = wv * XLOADS + i;             // LDS bytes [q*1024, q*1024+1024)
+        const int q = wv * XLOADS + i;               // LDS bytes [q*1024, q*1024+1024)
         const int r = q * (1024 / CB) + lane / PPR;  // tile row of this lane's 16 bytes
-        const int slot = lane % PPR;
-        const int c = slot ^ (r & 15);             // source piece for this slot
+        const int c = piece_slot<CB>(r, lane % PPR);  // source piece of this lane's slot
         const int rr = r < nvalid ? r : nvalid - 1;
         const uint8_t* src = a.X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.x + q * 1024), 16, 0, 0);
     }
     if (DT == RDG_FP8_E4M3) {
         // lanes 0..16*SPB-1 of wave w: row 16w + l/SPB, scale block SPB*kc + l%SPB
+        static_assert(TB == 16 * NW && SPB * 16 <= 64, "one load of scales per wave");
         const int l = lane % (16 * SPB);
         const int r = wv * 16 + l / SPB;
         const int rr = r < nvalid ? r : nvalid - 1;
@@ -196,14 +213,20 @@ template <int DT, bool GATED, bool SIGNAL>
 __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     using O = TOp<DT>;
     using op_t = typename O::op_t;
-    constexpr int S = O::STEPS;
+    constexpr int S = O::STEPS, NRT = O::NRT;
+    constexpr int PANEL = panel_rows<DT>();
+    constexpr int COLS = GATED ? PANEL / 2 : PANEL;  // output columns per workgroup
+    constexpr int NOT = GATED ? NRT / 2 : NRT;       // 16-column output tiles per wave
     constexpr bool FP8 = DT == RDG_FP8_E4M3;
     constexpr int CB = O::CB, CHUNK_LDS = TB * CB, SPB = CB / 128;
+    static_assert(!GATED || NRT % 2 == 0, "a gated wave holds its W1 and W3 tiles in pairs");
     __shared__ __attribute__((aligned(16))) uint8_t lx0[CHUNK_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t lx1[CHUNK_LDS];
     __shared__ __attribute__((aligned(16))) float ls0[FP8 ? TB * SPB : 4];
     __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * SPB : 4];
-    const Ring ring[2] = {{lx0, ls0}, {lx1, ls1}};
+    __shared__ __attribute__((aligned(16))) float lw0[FP8 ? NW * 2 * S : 4];
+    __shared__ __attribute__((aligned(16))) float lw1[FP8 ? NW * 2 * S : 4];
+    const Ring ring[2] = {{lx0, ls0, lw0}, {lx1, ls1, lw1}};
 
     int fb, tile;
     if (SIGNAL) {
@@ -213,7 +236,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         // keeps them in its L2
         fb = blockIdx.x;
         tile = blockIdx.y;
-        if (fb * PANEL >= a.Nout) return;  // padding workgroup (uniform)
+        if (fb * COLS >= a.Nout) return;  // padding workgroup (uniform)
     } else {
         // XCD-aware renumbering: hardware block b runs on XCD b % 8, which
         // gets ceil((total - x) / 8) blocks; give XCD x the contiguous logical
@@ -241,25 +264,31 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     const int nvalid = row_end - row0 < TB ? row_end - row0 : TB;
     const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // wave-uniform
     const int lane = lane_id();
-    // gated: 128 output features per workgroup, wave w: matrix w/4, features
-    // [f0 + 32(w%4), +32); down: 256 output columns, wave w: [f0 + 32w, +32)
-    const int f0 = fb * (GATED ? PANEL / 2 : PANEL);
-    const int mat = GATED ? wv / 4 : 0;
-    const int fw = f0 + (GATED ? (wv % 4) : wv) * 32;
+    // output columns [fw, fw + 16 NOT) of this wave
+    const int f0 = fb * COLS;
+    const int fw = f0 + wv * NOT * 16;
     const size_t xstride = (size_t)a.Kdim * O::ESZ;
     const int nks = a.Kdim / O::KS;
     const int nkb = a.Kdim / 128;
     const int nchunks = (int)(xstride / CB);
 
+    // weight tile rt: rows fw + 16 (rt % NOT) of W1 (gated, rt < NOT) or W3
+    // (gated, rt >= NOT) or W2 (down)
     const uint8_t* wt[NRT];
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-        const size_t grp = (size_t)e * (a.Nout / 16) + (fw + rt * 16) / 16;
-        wt[rt] = (mat == 0 ? a.Wa : a.Wb) + grp * nks * O::BLK;
+        const size_t grp = (size_t)e * (a.Nout / 16) + fw / 16 + rt % NOT;
+        wt[rt] = (rt < NOT ? a.Wa : a.Wb) + grp * nks * O::BLK;
     }
-    // fp8: this wave's weight block scales along K (its 32 rows lie in one 128-row block)
-    const float* wsc = nullptr;
-    if (FP8) wsc = (mat == 0 ? a.Was : a.Wbs) + ((size_t)e * (a.Nout / 128) + fw / 128) * nkb;
+    // fp8: the block scales along K of the wave's W1 / W2 rows and W3 rows
+    // (all within one 128-row block)
+    const float* wsa = nullptr;
+    const float* wsb = nullptr;
+    if (FP8) {
+        const size_t blk = ((size_t)e * (a.Nout / 128) + fw / 128) * nkb;
+        wsa = a.Was + blk;
+        wsb = GATED ? a.Wbs + blk : wsa;
+    }
 
     f32x4_t acc[NRT][NCT];
 #pragma unroll
@@ -267,15 +296,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) acc[rt][ct] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // two weight register sets (chunk k's and k+1's), three ring slots
+    // two weight register sets (chunk k's and k+1's); fp8: the chunk's
+    // weight block scales travel with the token chunk's ring slot (direct
+    // loads into LDS: a register load of them would make the compiler wait
+    // for the chunk in flight to copy it)
     op_t w[2][S][NRT];
-    float sw[2][S];
 
-    auto request_w = [&](int kc, op_t (&wr)[S][NRT], float (&swr)[S]) {
+    auto request_w = [&](int kc, op_t (&wr)[S][NRT], const Ring& rg) {
         O::load_w(wr, wt, kc * S, lane);
         if (FP8) {
-#pragma unroll
-            for (int s = 0; s < S; ++s) swr[s] = wsc[kc * S + s];
+            constexpr int NSC = GATED ? 2 * S : S;
+            const float* src = (lane < S ? wsa : wsb) + kc * S + lane % S;
+            if (lane < NSC)
+                __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(rg.w + wv * 2 * S), 4, 0, 0);
         }
     };
     // One chunk: items i = (step s, token tile ct) in order.  The token
@@ -283,16 +316,31 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // three-deep register ring), and fp8 promotes item i-1's block partials
     // behind item i's MFMAs; the scheduling barrier after each item keeps the
     // compiler from hoisting a chunk's worth of LDS reads (registers).
-    auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT], const float (&swr)[S]) {
+    auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT]) {
         constexpr int NI = S * NCT;
         op_t xb[3];
-        float fb[4];
+        float sx[4];
+        float swr[S][2];  // fp8: weight block scales of each step (W1 / W2, W3)
+        if (FP8) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                swr[s][0] = rg.w[wv * 2 * S + s];
+                swr[s][1] = GATED ? rg.w[wv * 2 * S + S + s] : swr[s][0];
+            }
+        }
         f32x4_t p[2][NRT];
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         auto fetch = [&](int i) {
             const int si = i / NCT, r = (i % NCT) * 16 + (lane & 15);
             xb[i % 3] = O::load_x(rg.x, r, si, lane >> 4);
-            if (FP8) fb[i % 4] = rg.s[r * SPB + si] * swr[si];
+            if (FP8) sx[i % 4] = rg.s[r * SPB + si];
+        };
+        auto promote = [&](int i) {  // fp8: item i's block partials into the accumulators
+            const int si = i / NCT, ct = i % NCT;
+            const float fa = sx[i % 4] * swr[si][0];
+            const float fb3 = sx[i % 4] * swr[si][1];
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt) acc[rt][ct] += p[i % 2][rt] * (rt < NOT ? fa : fb3);
         };
         fetch(0);
         fetch(1);
@@ -306,24 +354,21 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             } else {
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) p[i % 2][rt] = O::mma(z, wr[si][rt], xb[i % 3]);
-                if (i > 0) {
-                    const int cp = (i - 1) % NCT;
-#pragma unroll
-                    for (int rt = 0; rt < NRT; ++rt) acc[rt][cp] += p[(i - 1) % 2][rt] * fb[(i - 1) % 4];
-                }
+                // issued behind this item's MFMAs, so that the promotion runs
+                // while they execute (item i-1's partials are complete once
+                // the MFMA unit starts on item i's)
+                __builtin_amdgcn_sched_barrier(0);
+                if (i > 0) promote(i - 1);
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (FP8) {
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) acc[rt][NCT - 1] += p[(NI - 1) % 2][rt] * fb[(NI - 1) % 4];
-        }
+        if (FP8) promote(NI - 1);
     };
 
     // Chunk k+1's token rows and weights are requested once chunk k has
     // arrived, and are in flight while chunk k is multiplied.
     stage_chunk<DT>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
-    request_w(0, w[0], sw[0]);
+    request_w(0, w[0], ring[0]);
     for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -336,106 +381,89 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             lds_barrier();
             if (kc + 1 < nchunks) {
                 stage_chunk<DT>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
-                request_w(kc + 1, w[(j + 1) % 2], sw[(j + 1) % 2]);
+                request_w(kc + 1, w[(j + 1) % 2], ring[(j + 1) % 2]);
             }
-            compute(ring[j], w[j], sw[j]);
+            compute(ring[j], w[j]);
         }
     }
 
     // ---------------------------------------------------------------- epilogue
     // 16x16 accumulator tile: lane l holds column (row of the layout) l % 16 and
-    // rows (output features) 4*(l/16) .. +3
-    const int fl = fw + (lane >> 4) * 4;
-    __syncthreads();  // every wave is done with the ring
+    // rows (output features) 4*(l/16) .. +3; gated, the SiLU-gated product of
+    // tile ot is formed from W1 tile ot and W3 tile ot + NOT in place
     if (GATED) {
-        // the up-projection waves hand their accumulators to the gate waves,
-        // weight tile rt through ring slot rt: [4 feature groups][8][64 lanes]
-        if (mat == 1) {
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                f32x4_t* xch = reinterpret_cast<f32x4_t*>(rt == 0 ? lx0 : lx1);
+        for (int ot = 0; ot < NOT; ++ot)
 #pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) xch[((wv % 4) * NCT + ct) * kWave + lane] = acc[rt][ct];
-            }
-        }
-        __syncthreads();
-        if (mat == 0) {
+            for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
-                const f32x4_t* xch = reinterpret_cast<const f32x4_t*>(rt == 0 ? lx0 : lx1);
-#pragma unroll
-                for (int ct = 0; ct < NCT; ++ct) {
-                    const f32x4_t u = xch[((wv % 4) * NCT + ct) * kWave + lane];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float g = acc[rt][ct][r];
-                        acc[rt][ct][r] = g / (1.0f + __expf(-g)) * u[r];
-                    }
+                for (int r = 0; r < 4; ++r) {
+                    const float g = acc[ot][ct][r];
+                    acc[ot][ct][r] = g / (1.0f + __expf(-g)) * acc[ot + NOT][ct][r];
                 }
-            }
-        }
     }
+    const int fl = fw + (lane >> 4) * 4;
     if (FP8 && GATED) {
-        // h re-quantised with one fp32 scale per row and 128 features: amax
-        // over the four gate waves' 32 features each
-        __syncthreads();                              // the exchange area is read
-        float* red = reinterpret_cast<float*>(lx0);  // [4 feature groups][128 rows]
-        if (mat == 0) {
+        // h re-quantised with one fp32 scale per row and 128 features: the
+        // workgroup's waves hold 16 NOT features each
+        static_assert(!(FP8 && GATED) || NW * NOT * 16 == 128, "an fp8 gate/up workgroup covers one 1x128 block of h");
+        __syncthreads();                              // every wave is done with the ring
+        float* red = reinterpret_cast<float*>(lx0);  // [NW waves][128 rows]
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                float m = 0.0f;
+        for (int ct = 0; ct < NCT; ++ct) {
+            float m = 0.0f;
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
+            for (int ot = 0; ot < NOT; ++ot)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[rt][ct][r]));
-                m = fmaxf(m, __shfl_xor(m, 16));
-                m = fmaxf(m, __shfl_xor(m, 32));
-                if (lane < 16) red[(wv % 4) * TB + ct * 16 + lane] = m;
-            }
+                for (int r = 0; r < 4; ++r) m = fmaxf(m, fabsf(acc[ot][ct][r]));
+            m = fmaxf(m, __shfl_xor(m, 16));
+            m = fmaxf(m, __shfl_xor(m, 32));
+            if (lane < 16) red[wv * TB + ct * 16 + lane] = m;
         }
         __syncthreads();
-        if (mat == 0) {
 #pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-                const int c = ct * 16 + (lane & 15);
-                const float amax = fmaxf(fmaxf(red[c], red[TB + c]), fmaxf(red[2 * TB + c], red[3 * TB + c]));
-                if (c >= nvalid) continue;
-                const int row = row0 + c;
-                const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-                const float inv = 1.0f / sc;
+        for (int ct = 0; ct < NCT; ++ct) {
+            const int c = ct * 16 + (lane & 15);
+            float amax = red[c];
 #pragma unroll
-                for (int rt = 0; rt < NRT; ++rt) {
-                    uint32_t q = 0;
+            for (int q = 1; q < NW; ++q) amax = fmaxf(amax, red[q * TB + c]);
+            if (c >= nvalid) continue;
+            const int row = row0 + c;
+            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float inv = 1.0f / sc;
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float tq = fminf(fmaxf(acc[rt][ct][r] * inv, -448.0f), 448.0f);
-                        q |= f32_to_e4m3(tq) << (8 * r);
-                    }
-                    *reinterpret_cast<uint32_t*>(a.O + (size_t)row * a.Nout + fl + rt * 16) = q;
+            for (int ot = 0; ot < NOT; ++ot) {
+                uint32_t q = 0;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float tq = fminf(fmaxf(acc[ot][ct][r] * inv, -448.0f), 448.0f);
+                    q |= f32_to_e4m3(tq) << (8 * r);
                 }
-                if (wv == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = sc;
+                *reinterpret_cast<uint32_t*>(a.O + (size_t)row * a.Nout + fl + ot * 16) = q;
             }
+            if (wv == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = sc;
         }
-    } else if (mat == 0) {
+    } else {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const int c = ct * 16 + (lane & 15);
             if (c >= nvalid) continue;
             const int row = row0 + c;
 #pragma unroll
-            for (int rt = 0; rt < NRT; ++rt) {
+            for (int ot = 0; ot < NOT; ++ot) {
                 uint2 o;
-                o.x = f32_to_bf16(acc[rt][ct][0]) | (f32_to_bf16(acc[rt][ct][1]) << 16);
-                o.y = f32_to_bf16(acc[rt][ct][2]) | (f32_to_bf16(acc[rt][ct][3]) << 16);
-                *reinterpret_cast<uint2*>(a.O + ((size_t)row * a.Nout + fl + rt * 16) * 2) = o;
+                o.x = f32_to_bf16(acc[ot][ct][0]) | (f32_to_bf16(acc[ot][ct][1]) << 16);
+                o.y = f32_to_bf16(acc[ot][ct][2]) | (f32_to_bf16(acc[ot][ct][3]) << 16);
+                *reinterpret_cast<uint2*>(a.O + ((size_t)row * a.Nout + fl + ot * 16) * 2) = o;
             }
         }
     }
-    if (SIGNAL) signal_done(a.signals + row0 / TB, PANEL);
+    if (SIGNAL) signal_done(a.signals + row0 / TB, COLS);
 }
 
 template <int DT>
 hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
+    constexpr int PANEL = panel_rows<DT>();
     dim3 block(NW * 64);
     if (c.stages & 1) {
         TArgs g{c.offsets, c.masked_m, c.tile_off, c.n_local, c.H, c.I, c.n_tiles_max,
@@ -457,16 +485,21 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int DT>
+bool shapes_ok(int H, int I) {
+    constexpr int PANEL = panel_rows<DT>(), CB = TOp<DT>::CB, ESZ = TOp<DT>::ESZ;
+    return I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * ESZ) % CB == 0 && ((int64_t)I * ESZ) % CB == 0;
+}
+
 }  // namespace
 
-// bf16 / fp8 with I a multiple of 128 (the gate/up feature panel) and H a
-// multiple of 256 (the down column panel); both reduction dimensions in whole
-// chunks (512 bytes bf16, 256 bytes fp8).
+// bf16 / fp8 with I a multiple of the gate/up feature panel (bf16 256, fp8
+// 128) and H of the down column panel (bf16 512, fp8 256); both reduction
+// dimensions in whole chunks.
 bool tiled_supported(int dtype, int H, int I) {
-    const int esz = dtype == RDG_BF16 ? 2 : dtype == RDG_FP8_E4M3 ? 1 : 0;
-    const int cb = dtype == RDG_BF16 ? TOp<RDG_BF16>::CB : TOp<RDG_FP8_E4M3>::CB;
-    return esz > 0 && I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * esz) % cb == 0 &&
-           ((int64_t)I * esz) % cb == 0;
+    if (dtype == RDG_BF16) return shapes_ok<RDG_BF16>(H, I);
+    if (dtype == RDG_FP8_E4M3) return shapes_ok<RDG_FP8_E4M3>(H, I);
+    return false;
 }
 
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s) {
