@@ -3,6 +3,7 @@
  * mixture-of-experts layer on AMD MI355X (gfx950).
  *
  *   rdg_route        group-limited top-k gating
+ *   rdg_eplb_place   EPLB placement of experts and redundant copies (host)
  *   rdg_eplb_remap   logical -> physical expert remap (redundant experts)
  *   rdg_dispatch     token -> expert permutation into a contiguous or masked layout
  *   rdg_grouped_ffn  grouped gate/up GEMM + SiLU-gated product + down GEMM
@@ -126,6 +127,38 @@ int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, in
 int rdg_eplb_remap(const int32_t* ids, const int64_t* token_gidx, int T, int K, const int32_t* log2phy,
                    const int32_t* n_replica, int r_max, int n_logical, int phys_begin, int n_local,
                    int32_t* local_ids, rdg_stream_t stream);
+
+/* EPLB placement: where the logical experts and their redundant copies go
+ * ([LEP] "EPLB": the measured per-expert load becomes a new expert-to-GPU
+ * map, hierarchically -- groups spread over nodes, then each node's experts
+ * placed inside it -- with extra copies of the popular experts; [H100]
+ * "Expert-parallel load balancer": the busiest experts get the most copies,
+ * rare ones share a GPU with busier ones, any GPU count).  Host code, all
+ * pointers host pointers; no GPU work, no global state (thread-safe).
+ *   load        [n_logical] host, finite and >= 0: e.g. token counts summed by
+ *               the dispatch recorder (rdg_layout.expert_load), as doubles
+ *   n_groups    groups of n_logical/n_groups consecutive experts
+ *   n_nodes     nodes of n_gpus/n_nodes GPUs; the hierarchical placement is
+ *               used when n_groups is a multiple of n_nodes (> 1), else the
+ *               machine is placed as one node
+ *   n_physical  slots, n_physical/n_gpus per GPU (>= n_logical)
+ *   r_max       columns of log2phy
+ *   phy2log     [n_physical] host out: logical expert in each slot
+ *   log2phy     [n_logical, r_max] host out: physical id of each copy, -1 pad
+ *   n_replica   [n_logical] host out: copies per expert (>= 1)
+ *   gpu_load    [n_gpus] host out (may be NULL): the load each GPU receives
+ * Rules: (1) groups by decreasing summed load, each to the least-loaded node
+ * that still takes groups (each takes n_groups/n_nodes); (2) in each node,
+ * one copy per expert, then every spare slot to the expert with the largest
+ * load per copy; (3) copies (load / copies each) by decreasing load, each to
+ * the node's least-loaded GPU with a free slot, which gives it its next slot:
+ * physical id = GPU * (n_physical/n_gpus) + slot.  Ties go to the lower
+ * group, node, expert, copy or GPU index.  Returns RDG_EINVAL for shapes that
+ * do not divide as stated or loads that are negative or not finite, and
+ * RDG_ECAPACITY when an expert would need more than r_max copies (outputs
+ * then undefined). */
+int rdg_eplb_place(const double* load, int n_logical, int n_groups, int n_nodes, int n_gpus, int n_physical,
+                   int r_max, int32_t* phy2log, int32_t* log2phy, int32_t* n_replica, double* gpu_load);
 
 /* Bytes of rdg_layout.work for a dispatch of T tokens x K slots over n_local experts. */
 size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);

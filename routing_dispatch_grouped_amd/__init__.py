@@ -40,6 +40,7 @@ _LP = ctypes.POINTER(rdg_layout)
 
 _SIGS = {
     "rdg_route": ([_P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "rdg_eplb_place": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "rdg_eplb_remap": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "rdg_dispatch_workspace_bytes": ([_I, _I, _I], _SZ),
     "rdg_dispatch": ([_P, _P, _I, _I, _I, _P, _I, _LP, _P, _P, _P], _I),
@@ -129,6 +130,23 @@ def rdg_route(logits, n_group, topk_group, K, scale, topk_ids, topk_w, stream=No
     B, N = logits.shape
     _check(_lib.rdg_route(_ptr(logits), B, N, n_group, topk_group, K, scale, _ptr(topk_ids), _ptr(topk_w),
                           _stream(stream)), "rdg_route")
+
+
+def rdg_eplb_place(load, n_groups, n_nodes, n_gpus, n_physical, r_max):
+    """Host call on numpy arrays: load [n_logical] (converted to float64).
+    Returns (phy2log [n_physical] int32, log2phy [n_logical, r_max] int32,
+    n_replica [n_logical] int32, gpu_load [n_gpus] float64)."""
+    import numpy as np
+    load = np.ascontiguousarray(load, dtype=np.float64)
+    n = load.shape[0]
+    phy2log = np.empty(n_physical, np.int32)
+    log2phy = np.empty((n, r_max), np.int32)
+    n_replica = np.empty(n, np.int32)
+    gpu_load = np.empty(n_gpus, np.float64)
+    hp = lambda a: ctypes.c_void_p(a.ctypes.data)
+    _check(_lib.rdg_eplb_place(hp(load), n, n_groups, n_nodes, n_gpus, n_physical, r_max, hp(phy2log), hp(log2phy),
+                               hp(n_replica), hp(gpu_load)), "rdg_eplb_place")
+    return phy2log, log2phy, n_replica, gpu_load
 
 
 def rdg_eplb_remap(ids, token_gidx, log2phy, n_replica, phys_begin, n_local, local_ids, stream=None):

@@ -11,7 +11,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT = os.path.join(PKG, "librdg.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "quant.hip", "pack.hip", "ffn.hip", "ffn_tiled.hip", "combine.hip"]
+SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "quant.hip", "pack.hip", "ffn.hip", "ffn_tiled.hip", "combine.hip",
+           "eplb.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -23,12 +24,21 @@ FLAGS = [
 ]
 
 
+# host-only sources (no device code): the system C++ compiler, plain IEEE
+# double arithmetic
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-ffp-contract=off", "-Wall", "-I", INCLUDE, "-I", CSRC]
+
+
 def _compile(src):
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+    if src.endswith(".cpp"):
+        cmd = [CXX] + CXXFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
+        raise RuntimeError("compile failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))
     return obj
 
 
