@@ -39,7 +39,11 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode_bf16",
-                   choices=["decode_bf16", "tiny_fp32", "prefill_bf16", "decode_rank_fp8", "prefill_rank_fp8"])
+                   choices=["decode_bf16", "tiny_fp32", "prefill_bf16", "prefill_bf16_balanced", "decode_rank_fp8",
+                            "prefill_rank_fp8"])
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of the step captured in a HIP graph (full-layer workloads); the gate/up "
+                        "kernel's own time then comes from as many eager steps run after them")
     p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
@@ -232,11 +236,11 @@ class Bench:
         if timed:
             e0 = self.torch.cuda.Event(enable_timing=True)
             e1 = self.torch.cuda.Event(enable_timing=True)
-            e0.record(self.stream)
+            e0.record(self.torch.cuda.current_stream())
         rdg.rdg_grouped_gate_up(self.L, self.DT, cfg["H"], cfg["I"], self.x_perm, self.x_perm_s, self.W["W1"],
                                 self.W["W3"], self.S.get("W1"), self.S.get("W3"), self.h, self.h_s)
         if timed:
-            e1.record(self.stream)
+            e1.record(self.torch.cuda.current_stream())
             self.events.append((e0, e1))
 
     def _shared(self, x, x_s, T, stream=None):
@@ -253,9 +257,11 @@ class Bench:
             # at DeepSeek-V3 sizes the shared expert runs on a second stream,
             # overlapping routing, dispatch and the routed GEMMs, and the combine
             # waits for both; for the tiny layer the cross-stream wait costs
-            # more than the overlap saves, so it runs in line
+            # more than the overlap saves, so it runs in line.  (The stream is
+            # the current one, so that the step can also be captured.)
+            main = self.torch.cuda.current_stream()
             if self.overlap_shared:
-                self.side.wait_stream(self.stream)
+                self.side.wait_stream(main)
                 with self.torch.cuda.stream(self.side):
                     self._shared(self.x, None, self.T, stream=self.side)
             else:
@@ -265,7 +271,7 @@ class Bench:
             self._gate_up(timed)
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
             if self.overlap_shared:
-                self.stream.wait_stream(self.side)
+                main.wait_stream(self.side)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, self.ys, self.out, self.YDT)
             return
         plan = self.plan
@@ -321,11 +327,28 @@ def main():
     balance = float(counts.mean() / counts.max()) if counts.max() > 0 else 1.0
 
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        b.step(timed=True)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    if args.graph:
+        if b.rank:
+            raise SystemExit("--graph covers the full-layer workloads")
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            b.step()
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            graph.replay()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(args.steps):
+            b.step(timed=True)
+        torch.cuda.synchronize()
+    else:
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            b.step(timed=True)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
     gate_ms = float(np.mean([a.elapsed_time(e) for a, e in b.events]))
 
@@ -359,7 +382,7 @@ def main():
     conf = {"workload": args.workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
-            "load_balance_mean_over_max": round(balance, 4)}
+            "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph)}
     if "m_max" in cfg:
         conf["m_max"] = cfg["m_max"]
     if b.rank:

@@ -18,6 +18,10 @@ Five workloads, named by what they are:
 * ``prefill_bf16``   4096 tokens (two 2048-token sequences), same shapes,
                      bf16, contiguous layout; logits make expert popularity
                      Zipf(1.1) over a seeded permutation.
+* ``prefill_bf16_balanced`` the same prefill layer with i.i.d. N(0,1)
+                     logits: every token's choice is a random selection that
+                     follows the group-limited rule, the "simulated perfect
+                     EPLB" expert distribution (balanced in expectation).
 * ``decode_rank_fp8`` one decode rank's share with EPLB: 72 ranks x 4
                      physical experts (256 logical + 32 replicas), the
                      bottleneck rank receives 1024 token-expert rows; fp8
@@ -43,6 +47,8 @@ WORKLOADS = {
                         dtype="bf16", layout="masked", m_max=256, scale=1.0, logits="normal_bias"),
     "prefill_bf16": dict(wid=3, B=4096, H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048, shared_I=2048,
                          dtype="bf16", layout="contiguous", scale=1.0, logits="zipf", zipf_s=1.1),
+    "prefill_bf16_balanced": dict(wid=6, B=4096, H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048,
+                                  shared_I=2048, dtype="bf16", layout="contiguous", scale=1.0, logits="normal"),
     "decode_rank_fp8": dict(wid=4, B_global=72 * 128, n_ranks=72, n_local=4, n_redundant=32, rows=1024,
                             H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048, shared_I=0,
                             dtype="fp8", layout="masked", m_max=1024, scale=1.0, logits="zipf", zipf_s=1.1),

@@ -135,6 +135,13 @@ def test_prefill_bf16_workload():
     _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=32, seed=3)
 
 
+def test_prefill_bf16_balanced_workload():
+    # the "simulated perfect EPLB" distribution of the H100 deployment
+    # article's prefill evaluation: random group-limited choices
+    cfg = dict(synth.WORKLOADS["prefill_bf16_balanced"], name="prefill_bf16_balanced")
+    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=32, seed=4)
+
+
 # ---------------------------------------------------------------- rank shares
 def rank_share(cfg):
     """One rank's received tokens under the EPLB placement: route the global

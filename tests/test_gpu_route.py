@@ -35,7 +35,7 @@ def _check(logits_np, n_group, topk_group, K, scale=1.0):
     assert np.max(np.abs(gw.astype(np.float64) - rw) / np.maximum(np.abs(rw), 1e-30)) <= bound
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "decode_bf16", "prefill_bf16", "prefill_bf16_balanced"])
 def test_route_workloads(name):
     cfg = synth.WORKLOADS[name]
     print("route", name, flush=True)
