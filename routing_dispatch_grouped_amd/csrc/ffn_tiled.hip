@@ -40,6 +40,8 @@
 // run back to back on the same XCD and re-read the panel from its L2; the
 // signalled down stage instead runs tile-major, so that row tiles complete in
 // layout order while a combine polls them.
+#include <type_traits>
+
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -311,13 +313,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(rg.w + wv * 2 * S), 4, 0, 0);
         }
     };
-    // One chunk: items i = (step s, token tile ct) in order.  The token
-    // operand of item i+2 is read from LDS while item i's MFMAs run (a
-    // three-deep register ring), and fp8 promotes item i-1's block partials
-    // behind item i's MFMAs; the scheduling barrier after each item keeps the
-    // compiler from hoisting a chunk's worth of LDS reads (registers).
-    auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT]) {
-        constexpr int NI = S * NCT;
+    // One chunk over the first NV 16-row token tiles: items i = (step s,
+    // token tile ct) in order.  The token operand of item i+2 is read from
+    // LDS while item i's MFMAs run (a three-deep register ring), and fp8
+    // promotes item i-1's block partials behind item i's MFMAs; the
+    // scheduling barrier after each item keeps the compiler from hoisting a
+    // chunk's worth of LDS reads (registers).
+    auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT], auto nv) {
+        constexpr int NV = decltype(nv)::value;
+        constexpr int NI = S * NV;
         op_t xb[3];
         float sx[4];
         float swr[S][2];  // fp8: weight block scales of each step (W1 / W2, W3)
@@ -331,12 +335,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         f32x4_t p[2][NRT];
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         auto fetch = [&](int i) {
-            const int si = i / NCT, r = (i % NCT) * 16 + (lane & 15);
+            const int si = i / NV, r = (i % NV) * 16 + (lane & 15);
             xb[i % 3] = O::load_x(rg.x, r, si, lane >> 4);
             if (FP8) sx[i % 4] = rg.s[r * SPB + si];
         };
         auto promote = [&](int i) {  // fp8: item i's block partials into the accumulators
-            const int si = i / NCT, ct = i % NCT;
+            const int si = i / NV, ct = i % NV;
             const float fa = sx[i % 4] * swr[si][0];
             const float fb3 = sx[i % 4] * swr[si][1];
 #pragma unroll
@@ -346,7 +350,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         fetch(1);
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int si = i / NCT, ct = i % NCT;
+            const int si = i / NV, ct = i % NV;
             if (i + 2 < NI) fetch(i + 2);
             if (!FP8) {
 #pragma unroll
@@ -366,26 +370,37 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     };
 
     // Chunk k+1's token rows and weights are requested once chunk k has
-    // arrived, and are in flight while chunk k is multiplied.
-    stage_chunk<DT>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
-    request_w(0, w[0], ring[0]);
-    for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
+    // arrived, and are in flight while chunk k is multiplied.  A tile with
+    // fewer valid rows (an expert's last tile) only stages and multiplies
+    // the 16-row token tiles that hold them: wave w stages rows [16w, 16w+16).
+    auto main_loop = [&](auto nv) {
+        constexpr int NV = decltype(nv)::value;
+        if (wv < NV) stage_chunk<DT>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+        request_w(0, w[0], ring[0]);
+        for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int kc = kc0 + j;
-            if (kc >= nchunks) break;
-            // this wave's loads of chunk kc have landed, then every wave's; past
-            // the barrier every wave is also done with chunk kc-1, whose ring
-            // slot and weight set are refilled next
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
-            lds_barrier();
-            if (kc + 1 < nchunks) {
-                stage_chunk<DT>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
-                request_w(kc + 1, w[(j + 1) % 2], ring[(j + 1) % 2]);
+            for (int j = 0; j < 2; ++j) {
+                const int kc = kc0 + j;
+                if (kc >= nchunks) break;
+                // this wave's loads of chunk kc have landed, then every wave's;
+                // past the barrier every wave is also done with chunk kc-1, whose
+                // ring slot and weight set are refilled next
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+                lds_barrier();
+                if (kc + 1 < nchunks) {
+                    if (wv < NV) stage_chunk<DT>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
+                    request_w(kc + 1, w[(j + 1) % 2], ring[(j + 1) % 2]);
+                }
+                compute(ring[j], w[j], nv);
             }
-            compute(ring[j], w[j]);
         }
-    }
+    };
+    // (fp8: the full tile only -- a second copy of the loop does not fit its
+    // registers)
+    if (nvalid > 64 || FP8) main_loop(std::integral_constant<int, 8>{});
+    else if (nvalid > 32) main_loop(std::integral_constant<int, 4>{});
+    else if (nvalid > 16) main_loop(std::integral_constant<int, 2>{});
+    else main_loop(std::integral_constant<int, 1>{});
 
     // ---------------------------------------------------------------- epilogue
     // 16x16 accumulator tile: lane l holds column (row of the layout) l % 16 and
