@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rdg_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-F32, BF16, FP8 = 0, 1, 2
+F32, BF16, FP8, FP8_UE8M0 = 0, 1, 2, 3
 CONTIGUOUS, MASKED = 0, 1
 OK, EINVAL, ECAPACITY = 0, -1, -2
 
@@ -50,6 +50,7 @@ def lib():
         L.orc_fp8_encode.argtypes = [ctypes.c_double]
         L.orc_fp8_encode.restype = ctypes.c_uint8
         L.orc_quantize_fp8.argtypes = [P, i32, i32, i32, i32, P, P]
+        L.orc_quantize_fp8_ue8m0.argtypes = [P, i32, i32, i32, i32, P, P]
         L.orc_quantize_fp8.restype = i32
         L.orc_sigmoid.argtypes = [f32]
         L.orc_sigmoid.restype = f32
@@ -104,15 +105,17 @@ def fp8_encode(v):
     return np.array([f(float(x)) for x in v.ravel()], dtype=np.uint8).reshape(v.shape)
 
 
-def quantize_fp8(src, block_rows):
-    """src: float32 [rows, cols] or uint16 bf16 bits.  Returns (codes uint8, scales float32)."""
+def quantize_fp8(src, block_rows, ue8m0=False):
+    """src: float32 [rows, cols] or uint16 bf16 bits.  Returns (codes uint8,
+    scales float32); ue8m0: power-of-two scales."""
     src = np.ascontiguousarray(src)
     dt = F32 if src.dtype == np.float32 else BF16
     assert src.dtype in (np.float32, np.uint16)
     rows, cols = src.shape
     q = np.empty((rows, cols), dtype=np.uint8)
     s = np.empty(((rows + block_rows - 1) // block_rows, cols // 128), dtype=np.float32)
-    rc = lib().orc_quantize_fp8(_p(src), dt, rows, cols, block_rows, _p(q), _p(s))
+    f = lib().orc_quantize_fp8_ue8m0 if ue8m0 else lib().orc_quantize_fp8
+    rc = f(_p(src), dt, rows, cols, block_rows, _p(q), _p(s))
     if rc != OK:
         raise ValueError("orc_quantize_fp8: %d" % rc)
     return q, s

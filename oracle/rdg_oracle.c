@@ -38,7 +38,12 @@
 #define ORC_EINVAL (-1)
 #define ORC_ECAPACITY (-2)
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2 };
+/* ORC_FP8_UE8M0: e4m3 codes whose block scales are powers of two (an 8-bit
+ * exponent-only scale; the variant of the block-scaled fp8 GEMM that scaled
+ * matrix instructions consume directly) */
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_FP8 = 2, ORC_FP8_UE8M0 = 3 };
+
+static int is_fp8(int dt) { return dt == ORC_FP8 || dt == ORC_FP8_UE8M0; }
 enum { ORC_CONTIGUOUS = 0, ORC_MASKED = 1 };
 
 int orc_num_threads(void) {
@@ -123,15 +128,31 @@ uint8_t orc_fp8_encode(double v) {
     return (uint8_t)code;
 }
 
+/* Scale of an fp8 block whose largest magnitude is amax (1 for an all-zero
+ * block).  fp32 form: amax / 448, an fp32 division.  Power-of-two form: the
+ * smallest 2^k with amax / 2^k <= 448, found by exact comparisons of amax
+ * with 448 * 2^k (k kept in the 8-bit exponent's range, 2^-127 .. 2^127). */
+static float fp8_block_scale(float amax, int pow2) {
+    int k;
+    if (!(amax > 0.0f)) return 1.0f;
+    if (!pow2) return amax / 448.0f;
+    frexp((double)amax / 448.0, &k);          /* a first guess */
+    while (k > -127 && ldexp(448.0, k - 1) >= (double)amax) --k;
+    while (ldexp(448.0, k) < (double)amax) ++k;
+    if (k < -127) k = -127;
+    return (float)ldexp(1.0, k);
+}
+
 /* Block quantiser (the "1d2d" format of the masked fp8 grouped GEMM,
  * [SBO] section 3: 1-D activation scales, 2-D weight scales).  Reading of
  * the open constants: fp32 scale s = amax / 448 over the block (s = 1 when
- * the block is all zero), code = RNE(clamp(v / s, -448, 448)), the division
- * done in fp32.  Blocks are block_rows x 128 (1 x 128 for activations,
- * 128 x 128 for weights).  src_dt: ORC_F32 or ORC_BF16; rows, cols row-major.
- * Scales are [ceil(rows/block_rows), cols/128] row-major. */
-int orc_quantize_fp8(const void* src, int src_dt, int rows, int cols, int block_rows,
-                     uint8_t* q, float* scales) {
+ * the block is all zero), or with pow2 the power-of-two scale above;
+ * code = RNE(clamp(v / s, -448, 448)), the division done in fp32.  Blocks
+ * are block_rows x 128 (1 x 128 for activations, 128 x 128 for weights).
+ * src_dt: ORC_F32 or ORC_BF16; rows, cols row-major.  Scales are
+ * [ceil(rows/block_rows), cols/128] row-major. */
+static int quantize_fp8(const void* src, int src_dt, int rows, int cols, int block_rows, int pow2,
+                        uint8_t* q, float* scales) {
     int nbr, nbc;
     if (cols % 128 != 0 || rows <= 0 || block_rows <= 0) return ORC_EINVAL;
     nbr = (rows + block_rows - 1) / block_rows;
@@ -148,7 +169,7 @@ int orc_quantize_fp8(const void* src, int src_dt, int rows, int cols, int block_
                                                 : (float)orc_bf16_decode(((const uint16_t*)src)[(size_t)r * cols + c]);
                     if (fabsf(v) > amax) amax = fabsf(v);
                 }
-            s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            s = fp8_block_scale(amax, pow2);
             scales[(size_t)br * nbc + bc] = s;
             for (r = r0; r < r1; ++r)
                 for (c = bc * 128; c < bc * 128 + 128; ++c) {
@@ -162,6 +183,16 @@ int orc_quantize_fp8(const void* src, int src_dt, int rows, int cols, int block_
         }
     }
     return ORC_OK;
+}
+
+int orc_quantize_fp8(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
+                     float* scales) {
+    return quantize_fp8(src, src_dt, rows, cols, block_rows, 0, q, scales);
+}
+
+int orc_quantize_fp8_ue8m0(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
+                           float* scales) {
+    return quantize_fp8(src, src_dt, rows, cols, block_rows, 1, q, scales);
 }
 
 /* ------------------------------------------------------------------------
@@ -464,7 +495,7 @@ static void matvec(int dt, int rows_w, int Kd, const void* W, const float* w_s, 
     int j, k, b;
     for (j = 0; j < rows_w; ++j) {
         double acc = 0.0;
-        if (dt != ORC_FP8) {
+        if (!is_fp8(dt)) {
             for (k = 0; k < Kd; ++k) acc += load_elem(dt, W, (size_t)j * Kd + k) * a[k];
         } else {
             for (b = 0; b < Kd / 128; ++b) {
@@ -501,12 +532,13 @@ static void expert_ffn_row(int dt, int H, int I, const void* a_row, const float*
         for (i = 0; i < I; ++i) h[i] = orc_bf16_decode(orc_bf16_encode(h[i]));
     } else {
         /* re-quantise h with 1x128 blocks from its fp32 image (same rule as
-         * orc_quantize_fp8); the codes are kept as values in h */
+         * the block quantiser, in the layer's scale form); the codes are kept
+         * as values in h */
         for (b = 0; b < I / 128; ++b) {
             float amax = 0.0f, s;
             for (i = b * 128; i < b * 128 + 128; ++i)
                 if (fabsf((float)h[i]) > amax) amax = fabsf((float)h[i]);
-            s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            s = fp8_block_scale(amax, dt == ORC_FP8_UE8M0);
             hs[b] = s;
             for (i = b * 128; i < b * 128 + 128; ++i) {
                 float t = (float)h[i] / s;
@@ -516,7 +548,7 @@ static void expert_ffn_row(int dt, int H, int I, const void* a_row, const float*
             }
         }
     }
-    if (dt == ORC_FP8) {
+    if (is_fp8(dt)) {
         /* y = W2 . h with h as fp8 codes and scales hs */
         int j;
         for (j = 0; j < H; ++j) {
@@ -556,7 +588,9 @@ int orc_moe_layer(int dt, int H, int I, int K, const void* x, const float* x_sca
                   int sh_I, const int32_t* sel, int n_sel, int out_dt, void* out, double* y_rows) {
     size_t esz = dt == ORC_F32 ? 4 : (dt == ORC_BF16 ? 2 : 1);
     int maxI = I > sh_I ? I : sh_I;
-    if (H <= 0 || I <= 0 || K <= 0 || (dt == ORC_FP8 && (H % 128 || I % 128 || maxI > 64 * 128))) return ORC_EINVAL;
+    if (H <= 0 || I <= 0 || K <= 0 || dt < ORC_F32 || dt > ORC_FP8_UE8M0 ||
+        (is_fp8(dt) && (H % 128 || I % 128 || maxI > 64 * 128)))
+        return ORC_EINVAL;
 #pragma omp parallel
     {
         double* scratch = (double*)malloc(sizeof(double) * (3 * (size_t)maxI + H));
@@ -566,7 +600,7 @@ int orc_moe_layer(int dt, int H, int I, int K, const void* x, const float* x_sca
         for (int si = 0; si < n_sel; ++si) {
             int t = sel[si], k, j;
             const void* a_row = (const char*)x + (size_t)t * H * esz;
-            const float* a_s = dt == ORC_FP8 ? x_scales + (size_t)t * (H / 128) : NULL;
+            const float* a_s = is_fp8(dt) ? x_scales + (size_t)t * (H / 128) : NULL;
             for (j = 0; j < H; ++j) acc[j] = 0.0;
             if (shW1) {
                 expert_ffn_row(dt, H, sh_I, a_row, a_s, shW1, shW3, shW2, shs1, shs3, shs2, scratch, y);
@@ -579,8 +613,8 @@ int orc_moe_layer(int dt, int H, int I, int K, const void* x, const float* x_sca
                         for (j = 0; j < H; ++j) y_rows[((size_t)si * K + k) * H + j] = 0.0;
                     continue;
                 }
-                expert_ffn_row(dt, H, I, a_row, a_s, W1[e], W3[e], W2[e], dt == ORC_FP8 ? s1[e] : NULL,
-                               dt == ORC_FP8 ? s3[e] : NULL, dt == ORC_FP8 ? s2[e] : NULL, scratch, y);
+                expert_ffn_row(dt, H, I, a_row, a_s, W1[e], W3[e], W2[e], is_fp8(dt) ? s1[e] : NULL,
+                               is_fp8(dt) ? s3[e] : NULL, is_fp8(dt) ? s2[e] : NULL, scratch, y);
                 if (y_rows)
                     for (j = 0; j < H; ++j) y_rows[((size_t)si * K + k) * H + j] = y[j];
                 for (j = 0; j < H; ++j) acc[j] += (double)topk_w[(size_t)t * K + k] * y[j];

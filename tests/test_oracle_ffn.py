@@ -35,7 +35,7 @@ def _make(rng, dt, H, I, E, orc):
             d = {}
             dd = []
             for name, w in (("1", W1), ("3", W3), ("2", W2)):
-                q, s = orc.quantize_fp8(w, 128)
+                q, s = orc.quantize_fp8(w, 128, ue8m0=dt == orc.FP8_UE8M0)
                 d["W" + name] = q
                 d["s" + name] = s
                 dd.append(orc.fp8_decode(q) * np.repeat(np.repeat(s.astype(np.float64), 128, 0), 128, 1))
@@ -51,7 +51,7 @@ def _x(rng, dt, T, H, orc):
     xb = _bf16(x)
     if dt == orc.BF16:
         return xb, None, orc.bf16_decode(xb)
-    q, s = orc.quantize_fp8(xb, 1)
+    q, s = orc.quantize_fp8(xb, 1, ue8m0=dt == orc.FP8_UE8M0)
     return q, s, orc.fp8_decode(q) * np.repeat(s.astype(np.float64), 128, 1)
 
 
@@ -64,10 +64,15 @@ def _ref_ffn(dt, a, W1, W3, W2, orc):
         h = h.astype(np.float32).astype(np.float64)
     elif dt == orc.BF16:
         h = torch.from_numpy(h).to(torch.bfloat16).double().numpy()
-    else:  # 1x128 blocks along I, scale amax/448 in fp32, torch's e4m3fn cast
+    else:  # 1x128 blocks along I, scale amax/448 in fp32 (or the power of two
+        # 2^ceil(log2(amax/448))), torch's e4m3fn cast
         hf = torch.from_numpy(h.astype(np.float32)).view(h.shape[0], -1, 128)
-        s = hf.abs().amax(-1, keepdim=True) / 448.0
-        s = torch.where(s > 0, s, torch.ones_like(s))
+        amax = hf.abs().amax(-1, keepdim=True)
+        if dt == orc.FP8_UE8M0:
+            s = torch.exp2(torch.ceil(torch.log2(amax.double() / 448.0))).float()
+        else:
+            s = amax / 448.0
+        s = torch.where(amax > 0, s, torch.ones_like(s))
         q = (hf / s).clamp(-448, 448).to(torch.float8_e4m3fn).double()
         h = (q * s.double()).view(h.shape[0], -1).numpy()
     y = h @ W2.T
@@ -76,7 +81,7 @@ def _ref_ffn(dt, a, W1, W3, W2, orc):
     return torch.from_numpy(y).to(torch.bfloat16).double().numpy()
 
 
-@pytest.mark.parametrize("dt,tol", [(0, 1e-6), (1, 8e-3), (2, 8e-3)])
+@pytest.mark.parametrize("dt,tol", [(0, 1e-6), (1, 8e-3), (2, 8e-3), (3, 8e-3)])
 def test_expert_ffn_against_dense_matmul(orc, dt, tol):
     rng = np.random.default_rng(dt)
     T, H, I, E, K = 12, 256, 384, 3, 2
@@ -104,7 +109,7 @@ def test_swapped_gate_and_up_is_detected(orc):
     assert orc.rel_err(y[:, 0], wrong) > 1e-2
 
 
-@pytest.mark.parametrize("dt", [0, 1, 2])
+@pytest.mark.parametrize("dt", [0, 1, 2, 3])
 def test_linearity_power_of_two(orc, dt):
     # doubling W2 doubles every stored output exactly (all roundings commute
     # with a power-of-two scale; fp8 scales double exactly)
@@ -121,7 +126,7 @@ def test_linearity_power_of_two(orc, dt):
             return dict(W1=_bf16(W1), W3=_bf16(W3), W2=_bf16(w2))
         d = {}
         for n, w in (("1", W1), ("3", W3), ("2", w2)):
-            d["W" + n], d["s" + n] = orc.quantize_fp8(w, 128)
+            d["W" + n], d["s" + n] = orc.quantize_fp8(w, 128, ue8m0=dt == orc.FP8_UE8M0)
         return d
 
     x, xs, _ = _x(rng, dt, T, H, orc)
@@ -155,10 +160,10 @@ def test_identity_experts_and_unpermute(orc):
         assert np.array_equal(out1, yp[L1["pos"][:, 0]])
 
 
-@pytest.mark.parametrize("dt", [0, 1, 2])
+@pytest.mark.parametrize("dt", [0, 1, 2, 3])
 def test_definition_path_equals_layout_path(orc, dt):
     rng = np.random.default_rng(30 + dt)
-    T, H, I, E, K = 40, 256, 128 if dt != 2 else 256, 8, 3
+    T, H, I, E, K = 40, 256, 128 if dt < 2 else 256, 8, 3
     ex, _ = _make(rng, dt, H, I, E, orc)
     sh, _ = _make(rng, dt, H, I, 1, orc)
     x, xs, _ = _x(rng, dt, T, H, orc)

@@ -88,3 +88,45 @@ def test_quantiser_blocks(orc, block_rows):
     qb, sb = orc.quantize_fp8(xb.view(torch.int16).numpy().view(np.uint16), block_rows)
     qf, sf = orc.quantize_fp8(xb.float().numpy(), block_rows)
     assert np.array_equal(qb, qf) and np.array_equal(sb, sf)
+
+
+def test_ue8m0_scale_rule(orc):
+    # power-of-two block scales: the smallest 2^k with amax / 2^k <= 448,
+    # checked against the closed form 2^ceil(log2(amax / 448)) and by its
+    # defining inequalities; an all-zero block gets 1
+    rng = np.random.default_rng(8)
+    rows, cols = 64, 512
+    mag = 2.0 ** rng.uniform(-30, 30, (rows, 1))
+    x = (rng.standard_normal((rows, cols)) * mag).astype(np.float32)
+    x[3, 128:256] = 0.0
+    q, s = orc.quantize_fp8(x, 1, ue8m0=True)
+    amax = np.abs(x.reshape(rows, -1, 128)).max(-1).astype(np.float64)
+    s64 = s.astype(np.float64)
+    nz = amax > 0
+    assert (np.frexp(s64)[0] == 0.5).all()                        # powers of two
+    assert (amax[nz] / s64[nz] <= 448.0).all() and (amax[nz] / (s64[nz] / 2) > 448.0).all()
+    assert (s64[nz] == 2.0 ** np.ceil(np.log2(amax[nz] / 448.0))).all()
+    assert s[3, 1] == 1.0
+    # each element is the nearest representable after scaling
+    deq = orc.fp8_decode(q) * np.repeat(s64, 128, 1)
+    big = np.abs(x) > np.repeat(s64, 128, 1) * 2.0 ** -6
+    assert (np.abs(deq - x)[big] / np.abs(x)[big]).max() <= 2.0 ** -4 + 1e-12
+
+
+def test_ue8m0_matches_fp32_rule_at_exact_powers(orc):
+    # a block whose amax is 448 * 2^j has the same scale 2^j under both rules,
+    # hence the same codes; one ulp more moves the power-of-two scale up
+    rng = np.random.default_rng(9)
+    x = rng.uniform(-1, 1, (8, 256)).astype(np.float32)
+    for r in range(8):
+        j = r - 4
+        x[r, 7] = np.float32(448.0 * 2.0 ** j)
+        x[r, 128:] = np.clip(x[r, 128:], -0.5, 0.5) * np.float32(448.0 * 2.0 ** j)
+        x[r, 200] = np.nextafter(np.float32(448.0 * 2.0 ** j), np.float32(np.inf))
+    qa, sa = orc.quantize_fp8(x, 1)
+    qb, sb = orc.quantize_fp8(x, 1, ue8m0=True)
+    for r in range(8):
+        j = r - 4
+        assert sb[r, 0] == 2.0 ** j and sa[r, 0] == sb[r, 0]
+        assert np.array_equal(qa[r, :128], qb[r, :128])
+        assert sb[r, 1] == 2.0 ** (j + 1)
