@@ -44,6 +44,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time replays of the step captured in a HIP graph (full-layer workloads); the gate/up "
                         "kernel's own time then comes from as many eager steps run after them")
+    p.add_argument("--ue8m0", action="store_true",
+                   help="fp8 workloads with power-of-two block scales (scaled-MFMA path)")
     p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
@@ -88,7 +90,7 @@ def measured_traffic(workload):
 class Bench:
     """Buffers and the step of one workload."""
 
-    def __init__(self, name, dev):
+    def __init__(self, name, dev, ue8m0=False):
         import torch
 
         import routing_dispatch_grouped_amd as rdg
@@ -97,6 +99,13 @@ class Bench:
         self.name, self.dev = name, dev
         self.cfg = cfg = synth.WORKLOADS[name]
         self.DT = {"f32": rdg.RDG_F32, "bf16": rdg.RDG_BF16, "fp8": rdg.RDG_FP8_E4M3}[cfg["dtype"]]
+        # fp8 with power-of-two block scales: same codes and layouts, scales
+        # applied inside the scaled MFMA by the 128-row kernels
+        self.ue8m0 = ue8m0 and cfg["dtype"] == "fp8"
+        self.fp8 = cfg["dtype"] == "fp8"
+        self.quant = rdg.rdg_quantize_fp8_ue8m0 if self.ue8m0 else rdg.rdg_quantize_fp8
+        if self.ue8m0:
+            self.DT = rdg.RDG_FP8_E4M3_UE8M0
         self.sdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[cfg["dtype"]]
         self.ydt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
         self.YDT = rdg.RDG_F32 if cfg["dtype"] == "f32" else rdg.RDG_BF16
@@ -118,7 +127,7 @@ class Bench:
         W = {k: torch.empty(shape, dtype=self.sdt, device=self.dev)
              for k, shape in (("W1", (n, I, H)), ("W3", (n, I, H)), ("W2", (n, H, I)))}
         S = {}
-        if self.DT == rdg.RDG_FP8_E4M3:
+        if self.fp8:
             S = {k: torch.empty(shape, dtype=torch.float32, device=self.dev)
                  for k, shape in (("W1", (n, I // 128, H // 128)), ("W3", (n, I // 128, H // 128)),
                                   ("W2", (n, H // 128, I // 128)))}
@@ -128,7 +137,7 @@ class Bench:
                 src = w[k]
                 if S:
                     q = torch.empty(src.shape, dtype=torch.uint8, device=self.dev)
-                    rdg.rdg_quantize_fp8(src, rdg.RDG_F32, 128, q, S[k][j])
+                    self.quant(src, rdg.RDG_F32, 128, q, S[k][j])
                     src = q
                 rdg.rdg_pack_weights(src, self.DT, W[k][j])
             del w
@@ -138,7 +147,7 @@ class Bench:
         torch, rdg = self.torch, self.rdg
         q = torch.empty(x.shape, dtype=torch.uint8, device=self.dev)
         s = torch.empty((x.shape[0], x.shape[1] // 128), dtype=torch.float32, device=self.dev)
-        rdg.rdg_quantize_fp8(x, rdg.RDG_BF16, 1, q, s)
+        self.quant(x, rdg.RDG_BF16, 1, q, s)
         return q, s
 
     def _buffers(self, T, K, n_local, kind, block_m=128, m_max=0):
@@ -149,7 +158,7 @@ class Bench:
         self.x_perm = torch.empty((m_cap, H), dtype=self.sdt, device=self.dev)
         self.h = torch.empty((m_cap, I), dtype=self.sdt, device=self.dev)
         self.y = torch.empty((m_cap, H), dtype=self.ydt, device=self.dev)
-        fp8 = self.DT == rdg.RDG_FP8_E4M3
+        fp8 = self.fp8
         self.x_perm_s = torch.empty((m_cap, H // 128), dtype=torch.float32, device=self.dev) if fp8 else None
         self.h_s = torch.empty((m_cap, I // 128), dtype=torch.float32, device=self.dev) if fp8 else None
 
@@ -159,7 +168,7 @@ class Bench:
         self.Ls = rdg.Layout(rdg.RDG_CONTIGUOUS, 1, T, 1, self.dev, block_m=16, m_cap=T)
         self.hs = torch.empty((T, shI), dtype=self.sdt, device=self.dev)
         self.hs_s = (torch.empty((T, shI // 128), dtype=torch.float32, device=self.dev)
-                     if self.DT == rdg.RDG_FP8_E4M3 else None)
+                     if self.fp8 else None)
         self.ys = torch.empty((T, cfg["H"]), dtype=self.ydt, device=self.dev)
 
     def _setup_full(self):
@@ -310,7 +319,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    b = Bench(args.workload, dev)
+    b = Bench(args.workload, dev, ue8m0=args.ue8m0)
     rdg, cfg = b.rdg, b.cfg
     for _ in range(args.warmup):
         b.step()
@@ -383,6 +392,8 @@ def main():
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
             "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph)}
+    if b.fp8:
+        conf["fp8_scales"] = "ue8m0 (power of two)" if b.ue8m0 else "fp32"
     if "m_max" in cfg:
         conf["m_max"] = cfg["m_max"]
     if b.rank:

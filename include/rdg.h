@@ -51,7 +51,10 @@ enum {
     RDG_EUNSUPPORTED = -5  /* a valid but unimplemented combination of sizes / types */
 };
 
-enum { RDG_F32 = 0, RDG_BF16 = 1, RDG_FP8_E4M3 = 2 };   /* element types */
+/* element types.  RDG_FP8_E4M3_UE8M0: e4m3 codes whose block scales are
+ * powers of two (still stored as fp32 values 2^k; an 8-bit exponent-only
+ * scale, the form gfx950's scaled MFMA applies in hardware). */
+enum { RDG_F32 = 0, RDG_BF16 = 1, RDG_FP8_E4M3 = 2, RDG_FP8_E4M3_UE8M0 = 3 };
 enum { RDG_CONTIGUOUS = 0, RDG_MASKED = 1 };            /* layout kinds */
 
 /* A dispatch layout ([LEP] DeepEP modes paragraph: the contiguous layout
@@ -200,6 +203,11 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  * W2_s [n_local, H/128, I/128]; every 128-long partial product is scaled by
  * its activation and weight block scales in fp32; h is re-quantised to e4m3
  * with 1x128 scales (h_scales_ws [m_cap, I/128]); y is bf16.
+ * RDG_FP8_E4M3_UE8M0: the same with power-of-two scales everywhere (inputs
+ * from rdg_quantize_fp8_ue8m0, h re-quantised with power-of-two scales); the
+ * 128-row kernels hand the scales to the MFMA as 8-bit exponents, so the
+ * block products are accumulated in fp32 by the matrix core with no
+ * per-block promotion.
  *   h_ws      [m_cap, I] (dtype's storage: fp32 / bf16 / e4m3)
  *   y         [m_cap, H] fp32 (RDG_F32) or bf16
  *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype, H, I))] int32, zeroed by the
@@ -290,6 +298,14 @@ int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* to
  * cols must be a multiple of 128; block_rows is 1 or 128. */
 int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,
                      float* scales, rdg_stream_t stream);
+
+/* The same quantiser with power-of-two scales: scale = the smallest 2^k with
+ * amax / 2^k <= 448 (k in [-126, 127]; 1 for an all-zero block), stored as
+ * the fp32 value 2^k.  For RDG_FP8_E4M3_UE8M0 layers.  (A variant of the
+ * [SBO] section 3 block format: its scales as 8-bit exponents, the form that
+ * scaled matrix instructions take.) */
+int rdg_quantize_fp8_ue8m0(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,
+                           float* scales, rdg_stream_t stream);
 
 /* Fill n int32 words with value (a kernel, so it is safe inside captured graphs). */
 int rdg_fill_i32(int32_t* p, int32_t value, int64_t n, rdg_stream_t stream);

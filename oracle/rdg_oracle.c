@@ -131,15 +131,16 @@ uint8_t orc_fp8_encode(double v) {
 /* Scale of an fp8 block whose largest magnitude is amax (1 for an all-zero
  * block).  fp32 form: amax / 448, an fp32 division.  Power-of-two form: the
  * smallest 2^k with amax / 2^k <= 448, found by exact comparisons of amax
- * with 448 * 2^k (k kept in the 8-bit exponent's range, 2^-127 .. 2^127). */
+ * with 448 * 2^k, with k kept in [-126, 127] (a normal fp32, and within the
+ * 8-bit exponent-only scale's range). */
 static float fp8_block_scale(float amax, int pow2) {
     int k;
     if (!(amax > 0.0f)) return 1.0f;
     if (!pow2) return amax / 448.0f;
     frexp((double)amax / 448.0, &k);          /* a first guess */
-    while (k > -127 && ldexp(448.0, k - 1) >= (double)amax) --k;
+    while (k > -126 && ldexp(448.0, k - 1) >= (double)amax) --k;
     while (ldexp(448.0, k) < (double)amax) ++k;
-    if (k < -127) k = -127;
+    if (k < -126) k = -126;
     return (float)ldexp(1.0, k);
 }
 

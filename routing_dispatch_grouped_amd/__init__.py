@@ -12,7 +12,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "librdg.so")
 
 RDG_OK, RDG_EINVAL, RDG_ECAPACITY, RDG_ETIMEOUT, RDG_EHIP, RDG_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
-RDG_F32, RDG_BF16, RDG_FP8_E4M3 = 0, 1, 2
+RDG_F32, RDG_BF16, RDG_FP8_E4M3, RDG_FP8_E4M3_UE8M0 = 0, 1, 2, 3
 RDG_CONTIGUOUS, RDG_MASKED = 0, 1
 
 
@@ -52,6 +52,7 @@ _SIGS = {
     "rdg_signal_threshold": ([_I, _I], _I),
     "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I64, _I, _P], _I),
     "rdg_quantize_fp8": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
+    "rdg_quantize_fp8_ue8m0": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "rdg_fill_i32": ([_P, ctypes.c_int32, _I64, _P], _I),
     "rdg_packed_weight_bytes": ([_I, _I, _I, _I], _SZ),
     "rdg_pack_weights": ([_P, _I, _I, _I, _I, _P, _P], _I),
@@ -210,6 +211,12 @@ def rdg_quantize_fp8(src, src_dtype, block_rows, q, scales, stream=None):
     rows, cols = src.shape
     _check(_lib.rdg_quantize_fp8(_ptr(src), src_dtype, rows, cols, block_rows, _ptr(q), _ptr(scales),
                                  _stream(stream)), "rdg_quantize_fp8")
+
+
+def rdg_quantize_fp8_ue8m0(src, src_dtype, block_rows, q, scales, stream=None):
+    rows, cols = src.shape
+    _check(_lib.rdg_quantize_fp8_ue8m0(_ptr(src), src_dtype, rows, cols, block_rows, _ptr(q), _ptr(scales),
+                                       _stream(stream)), "rdg_quantize_fp8_ue8m0")
 
 
 def rdg_pack_weights(W, dtype, W_packed, stream=None):

@@ -120,6 +120,7 @@ int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, 
         case RDG_F32: esz = 4; break;
         case RDG_BF16: esz = 2; break;
         case RDG_FP8_E4M3:
+        case RDG_FP8_E4M3_UE8M0:
             esz = 1;
             if (H % 128 != 0) return RDG_EINVAL;
             if (T > 0 && (!x_scales || !x_perm_scales)) return RDG_EINVAL;
@@ -127,7 +128,7 @@ int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, 
         default: return RDG_EINVAL;
     }
     if (T > 0 && (!x || !ids || !x_perm || !aligned16(x) || !aligned16(x_perm))) return RDG_EINVAL;
-    return hip_rc(launch_dispatch(x, dtype == RDG_FP8_E4M3 ? x_scales : nullptr, H * esz, T, H, ids, K, *L, x_perm,
+    return hip_rc(launch_dispatch(x, esz == 1 ? x_scales : nullptr, H * esz, T, H, ids, K, *L, x_perm,
                                   x_perm_scales, stream));
 }
 
@@ -153,8 +154,11 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
                             const float* W1_s, const float* W3_s, const float* W2_s, void* h_ws, float* h_scales_ws,
                             void* y, int32_t* signals, int stages, rdg_stream_t stream) {
     if (!layout_ok(L) || H < 128 || H % 128 != 0 || I < 128 || I % 128 != 0) return RDG_EINVAL;
-    if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3) return RDG_EINVAL;
+    if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3 && dtype != RDG_FP8_E4M3_UE8M0)
+        return RDG_EINVAL;
     if (L->n_rows == 0) return RDG_OK;  // nothing dispatched: no rows, nothing to launch
+    const bool pow2 = dtype == RDG_FP8_E4M3_UE8M0;
+    if (pow2) dtype = RDG_FP8_E4M3;
     const bool fp8 = dtype == RDG_FP8_E4M3;
     if (!h_ws || !aligned16(h_ws) || (fp8 && !h_scales_ws)) return RDG_EINVAL;
     if (stages & 1) {
@@ -195,6 +199,7 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     c.y = y;
     c.signals = signals;
     c.stages = stages;
+    c.pow2 = pow2;
     return hip_rc(launch_ffn(c, stream));
 }
 
@@ -247,16 +252,26 @@ int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int blo
     if (rows < 0 || cols < 128 || cols % 128 != 0 || (block_rows != 1 && block_rows != 128)) return RDG_EINVAL;
     if (src_dtype != RDG_F32 && src_dtype != RDG_BF16) return RDG_EINVAL;
     if (rows > 0 && (!src || !q || !scales)) return RDG_EINVAL;
-    return hip_rc(launch_quantize(src, src_dtype, rows, cols, block_rows, q, scales, stream));
+    return hip_rc(launch_quantize(src, src_dtype, rows, cols, block_rows, false, q, scales, stream));
+}
+
+int rdg_quantize_fp8_ue8m0(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,
+                           float* scales, rdg_stream_t stream) {
+    if (rows < 0 || cols < 128 || cols % 128 != 0 || (block_rows != 1 && block_rows != 128)) return RDG_EINVAL;
+    if (src_dtype != RDG_F32 && src_dtype != RDG_BF16) return RDG_EINVAL;
+    if (rows > 0 && (!src || !q || !scales)) return RDG_EINVAL;
+    return hip_rc(launch_quantize(src, src_dtype, rows, cols, block_rows, true, q, scales, stream));
 }
 
 size_t rdg_packed_weight_bytes(int dtype, int n_mat, int rows, int cols) {
     if (n_mat < 0 || rows < 0 || cols < 0) return 0;
-    const size_t esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2 : dtype == RDG_FP8_E4M3 ? 1 : 0;
+    const size_t esz = dtype == RDG_F32 ? 4 : dtype == RDG_BF16 ? 2
+                     : (dtype == RDG_FP8_E4M3 || dtype == RDG_FP8_E4M3_UE8M0) ? 1 : 0;
     return esz * (size_t)n_mat * rows * cols;
 }
 
 int rdg_pack_weights(const void* W, int dtype, int n_mat, int rows, int cols, void* W_packed, rdg_stream_t stream) {
+    if (dtype == RDG_FP8_E4M3_UE8M0) dtype = RDG_FP8_E4M3;  // the same codes, packed alike
     if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3) return RDG_EINVAL;
     if (n_mat < 0 || rows < 0 || cols < 0 || rows % 16 != 0 || cols % 128 != 0) return RDG_EINVAL;
     if ((size_t)n_mat * rows * cols > 0 && (!W || !W_packed || !aligned16(W) || !aligned16(W_packed)))

@@ -127,6 +127,7 @@ struct KArgs {
     uint8_t* O;           // [rows, Nout]  (h, or y)
     float* Os;            // fp8 h scales [rows, Nout/128]
     int32_t* signals;     // [rows / BT]
+    int pow2;             // fp8: h re-quantised with power-of-two scales
 };
 
 template <int DT, int BT, bool GATED, bool SIGNAL>
@@ -284,7 +285,7 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
         for (int ct = 0; ct < NCT; ++ct) {
             const int row = row0 + ct * 16 + (lane & 15);
             if (row >= row_end) continue;
-            const float s = amax[ct] > 0.0f ? amax[ct] / 448.0f : 1.0f;
+            const float s = fp8_block_scale(amax[ct], a.pow2 != 0);
             const float inv = 1.0f / s;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
@@ -515,6 +516,7 @@ KArgs gate_up_args(const FfnCall& c) {
     g.O = static_cast<uint8_t*>(c.h);
     g.Os = c.h_s;
     g.signals = nullptr;
+    g.pow2 = c.pow2;
     return g;
 }
 

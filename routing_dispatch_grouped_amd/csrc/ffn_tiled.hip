@@ -68,29 +68,26 @@ __device__ __forceinline__ int piece_slot(int r, int c) {
     return CB >= 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
 }
 
-// Per type: NRT (16-row weight tiles per wave) and the chunk CB (bytes of
-// each row per chunk), sized so that two chunks of weights in registers, the
-// accumulators and the operand pipeline fit two waves per SIMD (bf16: 64
-// weight rows per wave, so each token operand read from LDS feeds four MFMAs;
-// fp8 keeps registers for the block partials it promotes); the MFMA step KS
-// (reduction elements), element size, the packed weight tile size BLK (see
-// pack.hip) and MFMA steps per chunk.
+// Per type: the MFMA step KS (reduction elements), element size, the packed
+// weight tile size BLK (see pack.hip), and the operand loads for a chunk of
+// S steps and CB bytes per row.
 template <int DT>
 struct TOp;
 
 template <>
 struct TOp<RDG_BF16> {
     using op_t = bf16x8_t;
-    static constexpr int NRT = 4, CB = 128;
-    static constexpr int KS = 32, ESZ = 2, BLK = 1024, STEPS = CB / (KS * ESZ);
-    __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
+    static constexpr int KS = 32, ESZ = 2, BLK = 1024;
+    template <int S, int NRT>
+    __device__ static void load_w(op_t (&w)[S][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s)
+        for (int s = 0; s < S; ++s)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
                 w[s][rt] = *reinterpret_cast<const bf16x8_t*>(wt[rt] + (size_t)(t0 + s) * BLK + lane * 16);
     }
     // token operand of step s for local row r, lane group g: 16-byte piece 4s+g
+    template <int CB>
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
         return *reinterpret_cast<const bf16x8_t*>(buf + r * CB + (piece_slot<CB>(r, s * 4 + g) << 4));
     }
@@ -102,11 +99,11 @@ struct TOp<RDG_BF16> {
 template <>
 struct TOp<RDG_FP8_E4M3> {
     using op_t = i32x8_t;
-    static constexpr int NRT = 2, CB = 256;
-    static constexpr int KS = 128, ESZ = 1, BLK = 2048, STEPS = CB / KS;  // steps = 1x128 scale blocks
-    __device__ static void load_w(op_t (&w)[STEPS][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
+    static constexpr int KS = 128, ESZ = 1, BLK = 2048;  // a step is one 1x128 scale block
+    template <int S, int NRT>
+    __device__ static void load_w(op_t (&w)[S][NRT], const uint8_t* const (&wt)[NRT], int t0, int lane) {
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s)
+        for (int s = 0; s < S; ++s)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt) {
                 const uint8_t* tile = wt[rt] + (size_t)(t0 + s) * BLK;
@@ -119,6 +116,7 @@ struct TOp<RDG_FP8_E4M3> {
             }
     }
     // 32 bytes: pieces 8s+2g and 8s+2g+1
+    template <int CB>
     __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
         const int c = s * 8 + g * 2;
         const i32x4_t a = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (piece_slot<CB>(r, c) << 4));
@@ -131,10 +129,38 @@ struct TOp<RDG_FP8_E4M3> {
     __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
         return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
     }
+    // with block scales as 8-bit exponents: each lane's scale applies to the
+    // 32 reduction elements it holds of its row of a (weights) / column of b
+    // (tokens) -- here the lanes of one row or column carry the same scale
+    __device__ static f32x4_t mma_scaled(f32x4_t c, op_t a, op_t b, int ea, int eb) {
+        return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, ea, 0, eb);
+    }
 };
 
-template <int DT>
-constexpr int panel_rows() { return NW * TOp<DT>::NRT * 16; }  // weight rows per workgroup
+// Tile shape: NRT 16-row weight tiles per wave and the chunk CB (bytes of
+// each row per chunk), sized so that two chunks of weights in registers, the
+// accumulators and the operand pipeline fit two waves per SIMD.  WIDE: 64
+// weight rows per wave, so each token operand read from LDS feeds four MFMAs
+// (bf16, and fp8 with power-of-two scales when the grid still fills the
+// chip); otherwise 32 rows (fp8 with fp32 scales keeps registers for the
+// block partials it promotes).
+template <int DT, bool WIDE>
+struct TShape;
+template <>
+struct TShape<RDG_BF16, true> {
+    static constexpr int NRT = 4, CB = 128;
+};
+template <>
+struct TShape<RDG_FP8_E4M3, false> {
+    static constexpr int NRT = 2, CB = 256;
+};
+template <>
+struct TShape<RDG_FP8_E4M3, true> {
+    static constexpr int NRT = 4, CB = 128;
+};
+
+template <int DT, bool WIDE>
+constexpr int panel_rows() { return NW * TShape<DT, WIDE>::NRT * 16; }  // weight rows per workgroup
 
 struct TArgs {
     const int32_t* offsets;
@@ -184,10 +210,10 @@ struct Ring {
 // loads per wave (rows past the tile's valid rows re-read the last valid row:
 // in bounds, never stored); fp8: one load of the chunk's activation scales of
 // 16 rows per wave.
-template <int DT>
+template <int DT, int CB>
 __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, int row0, int nvalid, int kc,
                                             const Ring& ring, int wv, int lane) {
-    constexpr int CB = TOp<DT>::CB, XLOADS = TB * CB / 1024 / NW, SPB = CB / 128;
+    constexpr int XLOADS = TB * CB / 1024 / NW, SPB = CB / 128;
     constexpr int PPR = CB / 16;  // 16-byte pieces per row
     static_assert(XLOADS >= 1 && 1024 % CB == 0 && XLOADS * NW * 1024 == TB * CB, "chunk shape");
 #pragma unroll
@@ -211,16 +237,20 @@ __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int 
     }
 }
 
-template <int DT, bool GATED, bool SIGNAL>
+// PW2 (fp8 with power-of-two block scales): the scales go into the scaled
+// MFMA as 8-bit exponents and the matrix core accumulates across blocks; no
+// per-block promotion.  WIDE: see TShape.
+template <int DT, bool GATED, bool SIGNAL, bool PW2, bool WIDE>
 __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     using O = TOp<DT>;
     using op_t = typename O::op_t;
-    constexpr int S = O::STEPS, NRT = O::NRT;
-    constexpr int PANEL = panel_rows<DT>();
+    constexpr int NRT = TShape<DT, WIDE>::NRT, CB = TShape<DT, WIDE>::CB;
+    constexpr int S = CB / (O::KS * O::ESZ);  // MFMA steps per chunk
+    constexpr int PANEL = panel_rows<DT, WIDE>();
     constexpr int COLS = GATED ? PANEL / 2 : PANEL;  // output columns per workgroup
     constexpr int NOT = GATED ? NRT / 2 : NRT;       // 16-column output tiles per wave
     constexpr bool FP8 = DT == RDG_FP8_E4M3;
-    constexpr int CB = O::CB, CHUNK_LDS = TB * CB, SPB = CB / 128;
+    constexpr int CHUNK_LDS = TB * CB, SPB = CB / 128;
     static_assert(!GATED || NRT % 2 == 0, "a gated wave holds its W1 and W3 tiles in pairs");
     __shared__ __attribute__((aligned(16))) uint8_t lx0[CHUNK_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t lx1[CHUNK_LDS];
@@ -305,7 +335,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     op_t w[2][S][NRT];
 
     auto request_w = [&](int kc, op_t (&wr)[S][NRT], const Ring& rg) {
-        O::load_w(wr, wt, kc * S, lane);
+        O::template load_w<S, NRT>(wr, wt, kc * S, lane);
         if (FP8) {
             constexpr int NSC = GATED ? 2 * S : S;
             const float* src = (lane < S ? wsa : wsb) + kc * S + lane % S;
@@ -316,7 +346,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // One chunk over the first NV 16-row token tiles: items i = (step s,
     // token tile ct) in order.  The token operand of item i+2 is read from
     // LDS while item i's MFMAs run (a three-deep register ring), and fp8
-    // promotes item i-1's block partials behind item i's MFMAs; the
+    // promotes item i-1's block partials behind item i's MFMAs (with
+    // power-of-two scales the MFMA applies them and accumulates itself); the
     // scheduling barrier after each item keeps the compiler from hoisting a
     // chunk's worth of LDS reads (registers).
     auto compute = [&](const Ring& rg, const op_t (&wr)[S][NRT], auto nv) {
@@ -332,11 +363,19 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 swr[s][1] = GATED ? rg.w[wv * 2 * S + S + s] : swr[s][0];
             }
         }
+        int ew[S][2];  // PW2: the weight scales as 8-bit exponents
+        if (PW2) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                ew[s][0] = e8m0_of(swr[s][0]);
+                ew[s][1] = e8m0_of(swr[s][1]);
+            }
+        }
         f32x4_t p[2][NRT];
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         auto fetch = [&](int i) {
             const int si = i / NV, r = (i % NV) * 16 + (lane & 15);
-            xb[i % 3] = O::load_x(rg.x, r, si, lane >> 4);
+            xb[i % 3] = O::template load_x<CB>(rg.x, r, si, lane >> 4);
             if (FP8) sx[i % 4] = rg.s[r * SPB + si];
         };
         auto promote = [&](int i) {  // fp8: item i's block partials into the accumulators
@@ -352,9 +391,14 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         for (int i = 0; i < NI; ++i) {
             const int si = i / NV, ct = i % NV;
             if (i + 2 < NI) fetch(i + 2);
-            if (!FP8) {
+            if constexpr (!FP8) {
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) acc[rt][ct] = O::mma(acc[rt][ct], wr[si][rt], xb[i % 3]);
+            } else if constexpr (PW2) {
+                const int eb = e8m0_of(sx[i % 4]);  // this lane's token row
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[rt][ct] = O::mma_scaled(acc[rt][ct], wr[si][rt], xb[i % 3], ew[si][rt < NOT ? 0 : 1], eb);
             } else {
 #pragma unroll
                 for (int rt = 0; rt < NRT; ++rt) p[i % 2][rt] = O::mma(z, wr[si][rt], xb[i % 3]);
@@ -366,7 +410,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             }
             __builtin_amdgcn_sched_barrier(0);
         }
-        if (FP8) promote(NI - 1);
+        if (FP8 && !PW2) promote(NI - 1);
     };
 
     // Chunk k+1's token rows and weights are requested once chunk k has
@@ -375,7 +419,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // the 16-row token tiles that hold them: wave w stages rows [16w, 16w+16).
     auto main_loop = [&](auto nv) {
         constexpr int NV = decltype(nv)::value;
-        if (wv < NV) stage_chunk<DT>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+        if (wv < NV) stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
         request_w(0, w[0], ring[0]);
         for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
 #pragma unroll
@@ -388,7 +432,8 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
                 lds_barrier();
                 if (kc + 1 < nchunks) {
-                    if (wv < NV) stage_chunk<DT>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
+                    if (wv < NV)
+                        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
                     request_w(kc + 1, w[(j + 1) % 2], ring[(j + 1) % 2]);
                 }
                 compute(ring[j], w[j], nv);
@@ -419,9 +464,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     }
     const int fl = fw + (lane >> 4) * 4;
     if (FP8 && GATED) {
-        // h re-quantised with one fp32 scale per row and 128 features: the
-        // workgroup's waves hold 16 NOT features each
-        static_assert(!(FP8 && GATED) || NW * NOT * 16 == 128, "an fp8 gate/up workgroup covers one 1x128 block of h");
+        // h re-quantised with one scale per row and 128 features: the
+        // workgroup's waves hold 16 NOT features each, WPB consecutive waves
+        // one 128-feature block
+        constexpr int WPB = 128 / (NOT * 16);  // waves per 128-feature block
+        static_assert(128 % (NOT * 16) == 0 && NW % WPB == 0, "whole 1x128 blocks of h per workgroup");
         __syncthreads();                              // every wave is done with the ring
         float* red = reinterpret_cast<float*>(lx0);  // [NW waves][128 rows]
 #pragma unroll
@@ -439,12 +486,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
             const int c = ct * 16 + (lane & 15);
-            float amax = red[c];
+            const int w0 = wv / WPB * WPB;
+            float amax = red[w0 * TB + c];
 #pragma unroll
-            for (int q = 1; q < NW; ++q) amax = fmaxf(amax, red[q * TB + c]);
+            for (int q = 1; q < WPB; ++q) amax = fmaxf(amax, red[(w0 + q) * TB + c]);
             if (c >= nvalid) continue;
             const int row = row0 + c;
-            const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+            const float sc = fp8_block_scale(amax, PW2);
             const float inv = 1.0f / sc;
 #pragma unroll
             for (int ot = 0; ot < NOT; ++ot) {
@@ -456,7 +504,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 }
                 *reinterpret_cast<uint32_t*>(a.O + (size_t)row * a.Nout + fl + ot * 16) = q;
             }
-            if (wv == 0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + f0 / 128] = sc;
+            if (wv == w0 && lane < 16) a.Os[(size_t)row * (a.Nout / 128) + fw / 128] = sc;
         }
     } else {
 #pragma unroll
@@ -476,15 +524,15 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     if (SIGNAL) signal_done(a.signals + row0 / TB, COLS);
 }
 
-template <int DT>
+template <int DT, bool PW2, bool WIDE>
 hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
-    constexpr int PANEL = panel_rows<DT>();
+    constexpr int PANEL = panel_rows<DT, WIDE>();
     dim3 block(NW * 64);
     if (c.stages & 1) {
         TArgs g{c.offsets, c.masked_m, c.tile_off, c.n_local, c.H, c.I, c.n_tiles_max,
                 static_cast<const uint8_t*>(c.x), c.x_s, static_cast<const uint8_t*>(c.W1),
                 static_cast<const uint8_t*>(c.W3), c.W1_s, c.W3_s, static_cast<uint8_t*>(c.h), c.h_s, nullptr};
-        k_ffn_tiled<DT, true, false><<<dim3(c.n_tiles_max, c.I / (PANEL / 2)), block, 0, s>>>(g);
+        k_ffn_tiled<DT, true, false, PW2, WIDE><<<dim3(c.n_tiles_max, c.I / (PANEL / 2)), block, 0, s>>>(g);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
@@ -493,16 +541,16 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
                 static_cast<const uint8_t*>(c.h), c.h_s, static_cast<const uint8_t*>(c.W2), nullptr, c.W2_s,
                 nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
         if (c.signals)
-            k_ffn_tiled<DT, false, true><<<dim3(round8(c.H / PANEL), c.n_tiles_max), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, true, PW2, WIDE><<<dim3(round8(c.H / PANEL), c.n_tiles_max), block, 0, s>>>(d);
         else
-            k_ffn_tiled<DT, false, false><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
+            k_ffn_tiled<DT, false, false, PW2, WIDE><<<dim3(c.n_tiles_max, c.H / PANEL), block, 0, s>>>(d);
     }
     return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool WIDE>
 bool shapes_ok(int H, int I) {
-    constexpr int PANEL = panel_rows<DT>(), CB = TOp<DT>::CB, ESZ = TOp<DT>::ESZ;
+    constexpr int PANEL = panel_rows<DT, WIDE>(), CB = TShape<DT, WIDE>::CB, ESZ = TOp<DT>::ESZ;
     return I % (PANEL / 2) == 0 && H % PANEL == 0 && ((int64_t)H * ESZ) % CB == 0 && ((int64_t)I * ESZ) % CB == 0;
 }
 
@@ -512,17 +560,24 @@ bool shapes_ok(int H, int I) {
 // 128) and H of the down column panel (bf16 512, fp8 256); both reduction
 // dimensions in whole chunks.
 bool tiled_supported(int dtype, int H, int I) {
-    if (dtype == RDG_BF16) return shapes_ok<RDG_BF16>(H, I);
-    if (dtype == RDG_FP8_E4M3) return shapes_ok<RDG_FP8_E4M3>(H, I);
+    if (dtype == RDG_BF16) return shapes_ok<RDG_BF16, true>(H, I);
+    if (dtype == RDG_FP8_E4M3 || dtype == RDG_FP8_E4M3_UE8M0) return shapes_ok<RDG_FP8_E4M3, false>(H, I);
     return false;
 }
 
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s) {
     if (c.n_tiles_max <= 0) return hipSuccess;
     if (!tiled_supported(c.dtype, c.H, c.I)) return hipErrorInvalidValue;
-    if (c.dtype == RDG_BF16) return launch_dt<RDG_BF16>(c, s);
-    if (c.dtype == RDG_FP8_E4M3) return launch_dt<RDG_FP8_E4M3>(c, s);
-    return hipErrorInvalidValue;
+    if (c.dtype == RDG_BF16) return launch_dt<RDG_BF16, false, true>(c, s);
+    if (c.dtype != RDG_FP8_E4M3) return hipErrorInvalidValue;
+    if (!c.pow2) return launch_dt<RDG_FP8_E4M3, false, false>(c, s);
+    // power-of-two scales: 64 weight rows per wave when the row tiles times
+    // the wider gate/up panels fill the CUs several times over, else 32.
+    // n_tiles_max bounds the tiles from the dispatched slots, which can be
+    // several times the rows that arrive (a rank's share), hence the margin.
+    const bool wide = shapes_ok<RDG_FP8_E4M3, true>(c.H, c.I) &&
+                      (int64_t)c.n_tiles_max * (c.I / (panel_rows<RDG_FP8_E4M3, true>() / 2)) >= 4 * 256;
+    return wide ? launch_dt<RDG_FP8_E4M3, true, true>(c, s) : launch_dt<RDG_FP8_E4M3, true, false>(c, s);
 }
 
 }  // namespace rdg

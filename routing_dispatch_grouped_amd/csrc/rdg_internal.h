@@ -53,6 +53,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
     return sign | code;
 }
 
+// Scale of an fp8 block whose largest magnitude is amax (1 for an all-zero
+// block): amax / 448 in fp32, or with pow2 the smallest power of two 2^k with
+// 448 * 2^k >= amax, k kept in [-126, 127] (a normal fp32 and a valid 8-bit
+// exponent-only scale).  With amax = (1 + m) 2^e the power-of-two form is
+// k = e - 8, or e - 7 when m > 0.75 (448 = 1.75 * 2^8): exact bit logic.
+__device__ __forceinline__ float fp8_block_scale(float amax, bool pow2) {
+    if (!(amax > 0.0f)) return 1.0f;
+    if (!pow2) return amax / 448.0f;
+    const uint32_t u = __float_as_uint(amax);
+    const int be = (int)(u >> 23);  // biased exponent; 0 for subnormal amax
+    int k = be - 127 - 8 + ((u & 0x7fffffu) > 0x600000u ? 1 : 0);
+    if (be == 0 || k < -126) k = -126;
+    return __uint_as_float((uint32_t)(k + 127) << 23);
+}
+
+// 8-bit exponent-only (E8M0) encoding of a power-of-two fp32 scale: its
+// biased exponent.
+__device__ __forceinline__ int e8m0_of(float pow2_scale) { return (int)(__float_as_uint(pow2_scale) >> 23); }
+
 // ---------------------------------------------------------------- waves
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t x) {
 #pragma unroll
@@ -116,8 +135,6 @@ hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, 
 hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 hipError_t launch_pack(const void* W, int dtype, int n_mat, int rows, int cols, void* P, hipStream_t s);
-hipError_t launch_quantize(const void* src, int src_dt, int rows, int cols, int block_rows, uint8_t* q,
-                           float* scales, hipStream_t s);
 
 // End of a signalled down-GEMM workgroup: publish `cols` finished output
 // columns of its row tile.  Every wave first waits for its own stores (they
@@ -154,8 +171,12 @@ struct FfnCall {
     void* y;
     int32_t* signals;
     int stages;  // bit 0: gate/up, bit 1: down
+    bool pow2;   // fp8 with power-of-two (E8M0) block scales: h re-quantised the same way, and the
+                 // 128-row kernels apply the scales inside the scaled MFMA
 };
 hipError_t launch_ffn(const FfnCall& c, hipStream_t s);
+hipError_t launch_quantize(const void* src, int src_dt, int rows, int cols, int block_rows, bool pow2, uint8_t* q,
+                           float* scales, hipStream_t s);
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s);  // bt == 128, bf16 / fp8
 bool tiled_supported(int dtype, int H, int I);                 // shapes the bt == 128 kernels take
 

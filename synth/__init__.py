@@ -136,12 +136,12 @@ def normal(wid, tensor, index, shape, std, device, dtype):
 
 def storage_dtype(cfg):
     torch = _torch()
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float32}[cfg["dtype"]]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.float32, "fp8u": torch.float32}[cfg["dtype"]]
 
 
 def activation_dtype(cfg):
     torch = _torch()
-    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16}[cfg["dtype"]]
+    return {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.bfloat16, "fp8u": torch.bfloat16}[cfg["dtype"]]
 
 
 def x(cfg, T, device="cpu", tensor=3):

@@ -17,7 +17,12 @@ def rdg():
 
 def dt_code(cfg):
     m = rdg()
-    return {"f32": m.RDG_F32, "bf16": m.RDG_BF16, "fp8": m.RDG_FP8_E4M3}[cfg["dtype"]]
+    return {"f32": m.RDG_F32, "bf16": m.RDG_BF16, "fp8": m.RDG_FP8_E4M3, "fp8u": m.RDG_FP8_E4M3_UE8M0}[cfg["dtype"]]
+
+
+def is_fp8(cfg):
+    """fp8 e4m3 layers: "fp8" (fp32 block scales) and "fp8u" (power-of-two block scales)."""
+    return cfg["dtype"] in ("fp8", "fp8u")
 
 
 def np_of(t):
@@ -36,7 +41,8 @@ def out_as_f64(arr):
 
 def torch_dtype(dt):
     m = rdg()
-    return {m.RDG_F32: torch.float32, m.RDG_BF16: torch.bfloat16, m.RDG_FP8_E4M3: torch.uint8}[dt]
+    return {m.RDG_F32: torch.float32, m.RDG_BF16: torch.bfloat16, m.RDG_FP8_E4M3: torch.uint8,
+            m.RDG_FP8_E4M3_UE8M0: torch.uint8}[dt]
 
 
 class ExpertSet:
@@ -55,7 +61,8 @@ class ExpertSet:
         I = cfg["shared_I"] if shared else cfg["I"]
         self.H, self.I = H, I
         n = len(self.ids)
-        self.fp8 = cfg["dtype"] == "fp8"
+        self.fp8 = is_fp8(cfg)
+        self.pow2 = cfg["dtype"] == "fp8u"
         sdt = torch.uint8 if self.fp8 else synth.storage_dtype(cfg)
         code = dt_code(cfg)
         self.W1 = torch.empty((n, I, H), dtype=sdt, device=device)
@@ -74,7 +81,8 @@ class ExpertSet:
             for name, dst, sc in (("W1", self.W1, self.s1), ("W3", self.W3, self.s3), ("W2", self.W2, self.s2)):
                 if self.fp8:
                     nat = self.codes[name][j]
-                    m.rdg_quantize_fp8(w[name], m.RDG_F32, 128, nat, sc[j])
+                    quant = m.rdg_quantize_fp8_ue8m0 if self.pow2 else m.rdg_quantize_fp8
+                    quant(w[name], m.RDG_F32, 128, nat, sc[j])
                 else:
                     nat = w[name]
                 m.rdg_pack_weights(nat, code, dst[j])
@@ -89,7 +97,7 @@ class ExpertSet:
             return {k: np_of(v) for k, v in w.items()}
         out = {}
         for name, key, dev_s in (("W1", "1", self.s1), ("W3", "3", self.s3), ("W2", "2", self.s2)):
-            q, s = oracle.quantize_fp8(np_of(w[name]), 128)
+            q, s = oracle.quantize_fp8(np_of(w[name]), 128, ue8m0=self.pow2)
             if check_codes:
                 assert np.array_equal(q, np_of(self.codes[name][j])), "device weight codes differ from the oracle's"
                 assert np.array_equal(s, np_of(dev_s[j])), "device weight scales differ from the oracle's"
@@ -97,14 +105,14 @@ class ExpertSet:
         return out
 
 
-def quantize_act(x):
-    """Device 1x128 quantisation of activations [T, H]."""
+def quantize_act(x, pow2=False):
+    """Device 1x128 quantisation of activations [T, H] (pow2: power-of-two scales)."""
     m = rdg()
     T, H = x.shape
     q = torch.empty((T, H), dtype=torch.uint8, device=x.device)
     s = torch.empty((T, H // 128), dtype=torch.float32, device=x.device)
     src_dt = m.RDG_BF16 if x.dtype == torch.bfloat16 else m.RDG_F32
-    m.rdg_quantize_fp8(x, src_dt, 1, q, s)
+    (m.rdg_quantize_fp8_ue8m0 if pow2 else m.rdg_quantize_fp8)(x, src_dt, 1, q, s)
     return q, s
 
 
@@ -124,7 +132,7 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
     x_perm_s = torch.empty((L.m_cap, H // 128), dtype=torch.float32, device=x.device) if x_s is not None else None
     m.rdg_dispatch(x, x_s, dt, local_ids, L, x_perm, x_perm_s)
     h = torch.empty((L.m_cap, I), dtype=sdt, device=x.device)
-    h_s = torch.empty((L.m_cap, I // 128), dtype=torch.float32, device=x.device) if dt == m.RDG_FP8_E4M3 else None
+    h_s = torch.empty((L.m_cap, I // 128), dtype=torch.float32, device=x.device) if is_fp8(cfg) else None
     ydt = torch.float32 if dt == m.RDG_F32 else torch.bfloat16
     y = torch.empty((L.m_cap, H), dtype=ydt, device=x.device)
     sig = None
@@ -173,7 +181,7 @@ def run_shared(cfg, x, x_s, shared):
     m.rdg_layout_dense(T, L)
     sdt = torch_dtype(dt)
     h = torch.empty((T, I), dtype=sdt, device=x.device)
-    h_s = torch.empty((T, I // 128), dtype=torch.float32, device=x.device) if dt == m.RDG_FP8_E4M3 else None
+    h_s = torch.empty((T, I // 128), dtype=torch.float32, device=x.device) if is_fp8(cfg) else None
     ydt = torch.float32 if dt == m.RDG_F32 else torch.bfloat16
     y = torch.empty((T, H), dtype=ydt, device=x.device)
     m.rdg_grouped_ffn(L, dt, H, I, x, x_s, shared.W1, shared.W3, shared.W2, shared.s1, shared.s3, shared.s2,
@@ -194,7 +202,7 @@ def check_layout(L, ref, ids_shape):
 def row_tolerance(cfg):
     """Per-token ||out-ref|| / ||ref|| bound: catches a missing or extra
     expert term in a token whose values are small next to the tensor's max."""
-    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 1e-1}[cfg["dtype"]]
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 1e-1, "fp8u": 1e-1}[cfg["dtype"]]
 
 
 def check_rows(got, ref, cfg, what=""):
@@ -210,4 +218,4 @@ def check_rows(got, ref, cfg, what=""):
 
 def tolerance(cfg):
     """Max relative error max|out-ref|/max|ref| allowed per tensor."""
-    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2}[cfg["dtype"]]
+    return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp8u": 6e-2}[cfg["dtype"]]

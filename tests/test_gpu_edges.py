@@ -23,10 +23,10 @@ def _cfg(dtype, H=512, I=256, N=8, K=2, wid=700):
 def _inputs(cfg, T):
     x = synth.x(cfg, T, device=DEV)
     x_s, xo, xo_s = None, np_of(x), None
-    if cfg["dtype"] == "fp8":
-        x, x_s = quantize_act(x)
+    if cfg["dtype"] in ("fp8", "fp8u"):
+        x, x_s = quantize_act(x, cfg["dtype"] == "fp8u")
         if T:
-            xo, xo_s = oracle.quantize_fp8(xo, 1)
+            xo, xo_s = oracle.quantize_fp8(xo, 1, ue8m0=cfg["dtype"] == "fp8u")
     return x, x_s, xo, xo_s
 
 
@@ -76,7 +76,7 @@ def test_masked_capacity_drop_through_the_layer(dtype):
     _compare(cfg, np_of(r["out"]), ref, "capacity drop %s" % dtype)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("T", [128, 256, 129])
 def test_one_expert_whole_tiles(dtype, T):
     """Every token to expert 2 of 4 with K = 1: exactly T/128 full tiles (T=129: one row past them)."""
@@ -95,7 +95,7 @@ def test_one_expert_whole_tiles(dtype, T):
     _compare(cfg, np_of(r["out"]), ref, "one expert %s T=%d" % (dtype, T))
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8", "fp8u"])
 def test_hidden_not_a_multiple_of_256(dtype):
     m = rdg()
     cfg = dict(_cfg(dtype, H=384, I=384, N=4, K=2, wid=730), n_group=2, topk_group=1)
@@ -110,3 +110,30 @@ def test_hidden_not_a_multiple_of_256(dtype):
     ref = oracle.moe_layer(dt_code(cfg), xo, ri, rw, [experts.oracle_expert(j) for j in range(cfg["N"])],
                            x_scales=xo_s)
     _compare(cfg, np_of(r["out"]), ref, "H=384 %s" % dtype)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+def test_fp8u_wide_panels(kind):
+    """fp8 with power-of-two scales and enough row tiles that the 128-row
+    kernels take 64 weight rows per wave (the row tiles times the 256-feature
+    gate/up panels reach four times the CU count): two experts of 9000 and
+    7463 rows (ragged last tiles), I = 2048, contiguous and masked; sampled
+    rows, including every expert's last rows, against the oracle."""
+    m = rdg()
+    cfg = _cfg("fp8u", H=1024, I=2048, N=2, K=1, wid=740 + kind)
+    counts = (9000, 7463)
+    T = sum(counts)
+    ids_np = np.concatenate([np.full(c, e, np.int32) for e, c in enumerate(counts)]).reshape(T, 1)
+    ids_np = ids_np[np.random.default_rng(kind).permutation(T)]
+    w_np = np.full((T, 1), 1.0, np.float32)
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    m_max = 9088 if kind == m.RDG_MASKED else 0
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), experts, kind,
+                   block_m=128, m_max=m_max)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    last = [int(np.flatnonzero(ids_np[:, 0] == e)[-j]) for e in range(2) for j in (1, 2, 3)]
+    sel = np.unique(np.concatenate([np.random.default_rng(9).choice(T, 40, replace=False), last])).astype(np.int32)
+    ref = oracle.moe_layer(dt_code(cfg), xo, ids_np, w_np, [experts.oracle_expert(e) for e in range(2)],
+                           x_scales=xo_s, sel=sel)
+    _compare(cfg, np_of(r["out"])[sel], ref, "fp8u wide kind=%d" % kind)

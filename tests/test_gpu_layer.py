@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth
-from harness import (DEV, ExpertSet, check_layout, check_rows, dt_code, np_of, out_as_f64, quantize_act, rdg,
+from harness import (DEV, ExpertSet, check_layout, check_rows, dt_code, is_fp8, np_of, out_as_f64, quantize_act, rdg,
                      run_routed, run_shared, tolerance)
 
 pytestmark = pytest.mark.gpu
@@ -51,9 +51,10 @@ def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
     x_s = None
     xo = np_of(x)
     xo_s = None
-    if dt == m.RDG_FP8_E4M3:
-        xq, x_s = quantize_act(x)
-        rq, rs = oracle.quantize_fp8(np_of(x), 1)
+    if is_fp8(cfg):
+        pow2 = cfg["dtype"] == "fp8u"
+        xq, x_s = quantize_act(x, pow2)
+        rq, rs = oracle.quantize_fp8(np_of(x), 1, ue8m0=pow2)
         assert np.array_equal(np_of(xq), rq) and np.array_equal(np_of(x_s), rs)
         x, xo, xo_s = xq, rq, rs
     N = cfg["N"]
@@ -84,7 +85,7 @@ def _small_cfg(dtype, N=32, n_group=4, topk_group=2, K=4, H=512, I=256, wid=100)
 
 # row tiles 16 / 32 / 64 are picked from the rows per expert (T*K/N): 40*4/32=5,
 # 300*4/32=37.5, 600*4/16=150; the ragged token counts leave partial tiles
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("B,N,kind", [(40, 32, 0), (300, 32, 0), (600, 16, 0), (40, 32, 1), (300, 32, 1),
                                       (600, 16, 1)])
 def test_small_layers(dtype, B, N, kind):
@@ -98,16 +99,16 @@ def test_small_layers(dtype, B, N, kind):
 # a dense expert of T rows (the shared expert): T <= 256 takes the skinny
 # kernels with 1, 2 or 4 16-row tiles per workgroup (several row groups and a
 # ragged tail at T = 100 and 256 - 3); larger T the 128-row tiled kernels
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("T", [1, 16, 29, 64, 100, 253, 300])
 def test_dense_expert(dtype, T):
     m = rdg()
     cfg = _small_cfg(dtype, H=1024, I=512, wid=400 + T)
     x = synth.x(cfg, T, device=DEV)
     x_s, xo, xo_s = None, np_of(x), None
-    if dtype == "fp8":
-        x, x_s = quantize_act(x)
-        xo, xo_s = oracle.quantize_fp8(xo, 1)
+    if is_fp8(cfg):
+        x, x_s = quantize_act(x, dtype == "fp8u")
+        xo, xo_s = oracle.quantize_fp8(xo, 1, ue8m0=dtype == "fp8u")
         assert np.array_equal(np_of(x), xo) and np.array_equal(np_of(x_s), xo_s)
     shared = ExpertSet(cfg, [0], shared=True)
     got = np_of(run_shared(cfg, x, x_s, shared))
@@ -180,8 +181,9 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
     T = len(share["tokens"])
     plan = share["plan"]
     x_bf = synth.x(cfg, T, device=DEV)
-    xq, x_s = quantize_act(x_bf)
-    rq, rs = oracle.quantize_fp8(np_of(x_bf), 1)
+    pow2 = cfg["dtype"] == "fp8u"
+    xq, x_s = quantize_act(x_bf, pow2)
+    rq, rs = oracle.quantize_fp8(np_of(x_bf), 1, ue8m0=pow2)
     assert np.array_equal(np_of(xq), rq) and np.array_equal(np_of(x_s), rs)
     ids_d = torch.from_numpy(share["ids"]).to(DEV)
     loc = torch.empty_like(ids_d)
@@ -200,7 +202,7 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
     check_layout(r["L"], ref_l, rloc.shape)
     sel = _sample(T, n_sample, seed)
     oe = [experts.oracle_expert(j) for j in range(plan["n_local"])]
-    ref = oracle.moe_layer(oracle.FP8, rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
+    ref = oracle.moe_layer(dt_code(cfg), rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
     got = np_of(r["out"])[sel]
     err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
     print("%s rows=%d tokens=%d rel_err=%.3e" % (cfg["name"], cfg["rows"], T, err), flush=True)
@@ -213,6 +215,18 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
 def test_decode_rank_fp8_workload():
     cfg = dict(synth.WORKLOADS["decode_rank_fp8"], name="decode_rank_fp8")
     _rank_layer(cfg, rdg().RDG_MASKED, m_max=cfg["m_max"])
+
+
+@pytest.mark.parametrize("name", ["decode_rank_fp8", "prefill_rank_fp8"])
+def test_rank_workloads_ue8m0(name):
+    # the rank shares with power-of-two block scales (scales applied inside
+    # the scaled MFMA by the 128-row kernels)
+    m = rdg()
+    cfg = dict(synth.WORKLOADS[name], name=name + "_ue8m0", dtype="fp8u")
+    if name == "decode_rank_fp8":
+        _rank_layer(cfg, m.RDG_MASKED, m_max=cfg["m_max"])
+    else:
+        _rank_layer(cfg, m.RDG_CONTIGUOUS, block_m=128, signals=True, concurrent=True)
 
 
 def _valid_rows(L):
@@ -256,7 +270,7 @@ def test_prefill_rank_fp8_workload_sbo():
           (same_h, same_y, len(diff_tok), len(share["tokens"])), flush=True)
     if len(diff_tok):
         sel = diff_tok[:8]
-        ref = oracle.moe_layer(oracle.FP8, rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
+        ref = oracle.moe_layer(dt_code(cfg), rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
         for name, rr in (("signalled", r), ("sequential", r2)):
             got = np_of(rr["out"])[sel]
             rel = np.linalg.norm(out_as_f64(got) - out_as_f64(ref), axis=1) / np.linalg.norm(out_as_f64(ref), axis=1)
@@ -286,7 +300,7 @@ def test_prefill_rank_fp8_workload_sbo():
 # select 16-, 32-, 64- (fp32) and 128-row (bf16/fp8) tiles; contiguous and
 # masked layouts.  The concurrent run must equal the sequential one bit for
 # bit and the oracle within tolerance.
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("B", [40, 300, 600])
 @pytest.mark.parametrize("kind", [0, 1])
 def test_sbo_small(dtype, B, kind):
@@ -300,9 +314,9 @@ def test_sbo_small(dtype, B, kind):
     loc = torch.from_numpy(loc_np).to(DEV)
     x = synth.x(cfg, B, device=DEV)
     x_s, xo, xo_s = None, np_of(x), None
-    if dtype == "fp8":
-        x, x_s = quantize_act(x)
-        xo, xo_s = oracle.quantize_fp8(xo, 1)
+    if is_fp8(cfg):
+        x, x_s = quantize_act(x, dtype == "fp8u")
+        xo, xo_s = oracle.quantize_fp8(xo, 1, ue8m0=dtype == "fp8u")
     experts = ExpertSet(cfg, range(p0, p0 + n_local))
     m_max = ((B + 127) // 128) * 128 if kind == m.RDG_MASKED else 0
     seq = run_routed(cfg, x, x_s, loc, w, experts, kind, block_m=128, m_max=m_max)
