@@ -170,6 +170,9 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     }
     const FfnPlan plan = plan_ffn(L, dtype, H, I);
     const int bt = plan.bt;
+    // the skinny kernels run tile-major too (row tiles on grid y); they are
+    // chosen for at most 24 rows per expert, so this bound is never near
+    if (plan.nr > 0 && ffn_tiles_max(L, bt) > 65535) return RDG_EUNSUPPORTED;
     if (signals) {
         const int align = L->n_local == 1 ? 128 : L->kind == RDG_CONTIGUOUS ? L->block_m : L->m_max;
         if (align % bt != 0) return RDG_EUNSUPPORTED;

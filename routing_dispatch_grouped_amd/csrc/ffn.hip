@@ -328,11 +328,15 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
 // Skinny variant for weight-streaming row tiles (decode: a few tokens per
 // expert; a dense expert of up to a few hundred tokens).  Each workgroup owns
 // 16*FPW weight rows of one expert and NR consecutive 16-row tiles of its
-// tokens (BT = 16*NR rows); its four waves split the reduction dimension in
-// four contiguous ranges of 128-wide blocks, and the partial sums are added
-// in LDS in wave order (so the result does not depend on timing).  Many short
-// workgroups instead of few long ones keep the last round of the grid from
-// idling most of the GPU.  With NR = 1 an expert's weights are read once per
+// tokens (BT = 16*NR rows); its four waves split the reduction dimension by
+// 128-wide blocks, interleaved (wave w takes blocks w, w+4, ...), so that
+// the workgroup's loads run through each weight stream in order, and the
+// partial sums are added in LDS in wave order (so the result does not depend
+// on timing).  The grid is tile-major: the column blocks of one row tile are
+// consecutive workgroups, which stream neighbouring weight panels of one
+// expert and share its token rows in L2 (and signalled row tiles complete in
+// layout order).  Many short workgroups instead of few long ones keep the
+// last round of the grid from idling most of the GPU.  With NR = 1 an expert's weights are read once per
 // 16-row tile and are streamed past the caches; with NR > 1 the row groups of
 // one weight panel re-read it, so the loads stay cacheable.  Used for every
 // type except the fp8 gate/up stage, whose 1x128 re-quantisation of h needs
@@ -352,9 +356,8 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     static_assert(DT == RDG_FP8_E4M3 || 128 % (KS * U) == 0, "KS * U must divide 128");
     __shared__ f32x4_t part[4][FPW * G * NR][kWave];
 
-    // signalled: tile-major order (grid x = column block), so that row tiles
-    // complete in layout order for the polling consumer
-    const int tile = SIGNAL ? blockIdx.y : blockIdx.x;
+    // tile-major order (grid x = column block)
+    const int tile = blockIdx.y;
     const int n_tiles = a.tile_off[a.n_local];
     if (tile >= n_tiles) return;  // workgroup-uniform
     int lo = 0, hi = a.n_local;
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     const int e = lo;
     const int row0 = a.offsets[e] + (tile - a.tile_off[e]) * BT;
     const int row_end = a.offsets[e] + a.masked_m[e];
-    const int f0 = (SIGNAL ? blockIdx.x : blockIdx.y) * (16 * FPW);
+    const int f0 = blockIdx.x * (16 * FPW);
     if (f0 >= a.Nout) return;  // signalled grids are padded to a multiple of 8 column blocks (uniform)
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const size_t wstride = (size_t)a.Kdim * ESZ;
@@ -400,14 +403,13 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
             accB[rt][nr] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
     const int nkb = a.Kdim / 128;
-    const int kb0 = (wv * nkb) / 4, kb1 = ((wv + 1) * nkb) / 4;
     const float* was = nullptr;
     const float* wbs = nullptr;
     if (DT == RDG_FP8_E4M3) {
         was = a.Was + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
         if (GATED) wbs = a.Wbs + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
     }
-    for (int kb = kb0; kb < kb1; ++kb) {
+    for (int kb = wv; kb < nkb; kb += 4) {
         if (DT != RDG_FP8_E4M3) {
 #pragma unroll
             for (int k0 = kb * 128; k0 < kb * 128 + 128; k0 += KS * U) {
@@ -553,9 +555,9 @@ hipError_t launch_skinny(const FfnCall& c, hipStream_t s) {
         if constexpr (DT == RDG_FP8_E4M3) {
             k_ffn<DT, BT, true, false><<<dim3(c.n_tiles_max, c.I / 128), block, 0, s>>>(g);
         } else if constexpr (NR == 1) {
-            k_ffn_skinny<DT, true, false, 2, NR><<<dim3(c.n_tiles_max, c.I / 32), block, 0, s>>>(g);
+            k_ffn_skinny<DT, true, false, 2, NR><<<dim3(c.I / 32, c.n_tiles_max), block, 0, s>>>(g);
         } else {
-            k_ffn_skinny<DT, true, false, 1, NR><<<dim3(c.n_tiles_max, c.I / 16), block, 0, s>>>(g);
+            k_ffn_skinny<DT, true, false, 1, NR><<<dim3(c.I / 16, c.n_tiles_max), block, 0, s>>>(g);
         }
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -565,7 +567,7 @@ hipError_t launch_skinny(const FfnCall& c, hipStream_t s) {
         if (c.signals)
             k_ffn_skinny<DT, false, true, 2, NR><<<dim3(round8(c.H / 32), c.n_tiles_max), block, 0, s>>>(d);
         else
-            k_ffn_skinny<DT, false, false, 2, NR><<<dim3(c.n_tiles_max, c.H / 32), block, 0, s>>>(d);
+            k_ffn_skinny<DT, false, false, 2, NR><<<dim3(c.H / 32, c.n_tiles_max), block, 0, s>>>(d);
     }
     return hipGetLastError();
 }
