@@ -46,6 +46,9 @@ def parse():
                         "kernel's own time then comes from as many eager steps run after them")
     p.add_argument("--ue8m0", action="store_true",
                    help="fp8 workloads with power-of-two block scales (scaled-MFMA path)")
+    p.add_argument("--tbo", action="store_true",
+                   help="prefill layers as two micro-batches cut at a sequence boundary, on two streams "
+                        "(the roofline then covers micro-batch A's gate/up)")
     p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
@@ -90,7 +93,7 @@ def measured_traffic(workload):
 class Bench:
     """Buffers and the step of one workload."""
 
-    def __init__(self, name, dev, ue8m0=False):
+    def __init__(self, name, dev, ue8m0=False, tbo=False):
         import torch
 
         import routing_dispatch_grouped_amd as rdg
@@ -112,10 +115,13 @@ class Bench:
         self.events = []
         self.stream = torch.cuda.current_stream()
         self.rank = "B_global" in cfg
+        self.tbo = None
         if self.rank:
             self._setup_rank()
         else:
             self._setup_full()
+            if tbo:
+                self._setup_tbo()
 
     # ------------------------------------------------------------ weights
     def _experts(self, ids, shared=False):
@@ -188,6 +194,65 @@ class Bench:
         self.side = torch.cuda.Stream()
         self.overlap_shared = cfg["H"] >= 1024
         self.out = torch.empty((B, cfg["H"]), dtype=self.ydt, device=self.dev)
+
+    def _setup_tbo(self):
+        """Two micro-batches cut at a sequence boundary (rdg_tbo_split), each with
+        its own layout and buffers; the second runs on a stream of its own."""
+        torch, rdg, cfg = self.torch, self.rdg, self.cfg
+        if "seq_lens" not in cfg:
+            raise SystemExit("--tbo needs a workload made of sequences (the prefill layers)")
+        lens = cfg["seq_lens"]
+        cut = sum(lens[:rdg.rdg_tbo_split(lens)])
+        H, I, K, N = cfg["H"], cfg["I"], cfg["K"], cfg["N"]
+        self.tbo = []
+        for t0, t1 in ((0, cut), (cut, self.T)):
+            T = t1 - t0
+            L = rdg.Layout(rdg.RDG_CONTIGUOUS, N, T, K, self.dev, block_m=128)
+            mb = dict(t0=t0, T=T, L=L, x=self.x[t0:t1], logits=self.logits[t0:t1], ids=self.ids[t0:t1],
+                      tw=self.tw[t0:t1], out=self.out[t0:t1], ys=self.ys[t0:t1],
+                      x_perm=torch.empty((L.m_cap, H), dtype=self.sdt, device=self.dev),
+                      h=torch.empty((L.m_cap, I), dtype=self.sdt, device=self.dev),
+                      y=torch.empty((L.m_cap, H), dtype=self.ydt, device=self.dev))
+            self.tbo.append(mb)
+        self.tbo_stream = torch.cuda.Stream()
+        self.L = self.tbo[0]["L"]   # statistics and the roofline: micro-batch A
+
+    def _step_tbo(self, timed):
+        """Shared expert on the side stream; micro-batch A's stages on this
+        stream and B's on another, issued alternately so that each one's
+        routing, dispatch and combine can run beside the other's GEMMs."""
+        rdg, cfg, torch = self.rdg, self.cfg, self.torch
+        H, I, K = cfg["H"], cfg["I"], cfg["K"]
+        main = torch.cuda.current_stream()
+        self.side.wait_stream(main)
+        self.tbo_stream.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            self._shared(self.x, None, self.T, stream=self.side)
+        A, B = self.tbo
+        sB = self.tbo_stream
+        for mb, st in ((A, main), (B, sB)):
+            with torch.cuda.stream(st):
+                rdg.rdg_route(mb["logits"], cfg["n_group"], cfg["topk_group"], K, cfg["scale"], mb["ids"], mb["tw"],
+                              stream=st)
+                rdg.rdg_dispatch(mb["x"], None, self.DT, mb["ids"], mb["L"], mb["x_perm"], stream=st)
+        for mb, st in ((A, main), (B, sB)):
+            with torch.cuda.stream(st):
+                if timed and mb is A:
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record(st)
+                rdg.rdg_grouped_gate_up(mb["L"], self.DT, H, I, mb["x_perm"], None, self.W["W1"], self.W["W3"], None,
+                                        None, mb["h"], None, stream=st)
+                if timed and mb is A:
+                    e1.record(st)
+                    self.events.append((e0, e1))
+                rdg.rdg_grouped_down(mb["L"], self.DT, H, I, mb["h"], None, self.W["W2"], None, mb["y"], stream=st)
+        for mb, st in ((A, main), (B, sB)):
+            with torch.cuda.stream(st):
+                st.wait_stream(self.side)
+                rdg.rdg_combine(mb["y"], self.YDT, mb["L"], mb["tw"], mb["T"], K, H, mb["ys"], mb["out"], self.YDT,
+                                stream=st)
+        main.wait_stream(sB)
 
     def _setup_rank(self):
         """One rank's received share: the global batch is routed and remapped on
@@ -262,6 +327,8 @@ class Bench:
     def step(self, timed=False):
         rdg, cfg = self.rdg, self.cfg
         H, I, K = cfg["H"], cfg["I"], cfg["K"]
+        if self.tbo:
+            return self._step_tbo(timed)
         if not self.rank:
             # at DeepSeek-V3 sizes the shared expert runs on a second stream,
             # overlapping routing, dispatch and the routed GEMMs, and the combine
@@ -319,7 +386,7 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    b = Bench(args.workload, dev, ue8m0=args.ue8m0)
+    b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo)
     rdg, cfg = b.rdg, b.cfg
     for _ in range(args.warmup):
         b.step()
@@ -392,6 +459,8 @@ def main():
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
             "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph)}
+    if b.tbo:
+        conf["tbo_micro_batches"] = [mb["T"] for mb in b.tbo]
     if b.fp8:
         conf["fp8_scales"] = "ue8m0 (power of two)" if b.ue8m0 else "fp32"
     if "m_max" in cfg:

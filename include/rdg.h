@@ -5,6 +5,7 @@
  *   rdg_route        group-limited top-k gating
  *   rdg_eplb_place   EPLB placement of experts and redundant copies (host)
  *   rdg_eplb_remap   logical -> physical expert remap (redundant experts)
+ *   rdg_tbo_split    two-batch-overlap cut of a batch into micro-batches (host)
  *   rdg_dispatch     token -> expert permutation into a contiguous or masked layout
  *   rdg_grouped_ffn  grouped gate/up GEMM + SiLU-gated product + down GEMM
  *   rdg_combine      routing-weighted unpermute-and-sum (optionally polling
@@ -162,6 +163,17 @@ int rdg_eplb_remap(const int32_t* ids, const int64_t* token_gidx, int T, int K, 
  * then undefined). */
 int rdg_eplb_place(const double* load, int n_logical, int n_groups, int n_nodes, int n_gpus, int n_physical,
                    int r_max, int32_t* phy2log, int32_t* log2phy, int32_t* n_replica, double* gpu_load);
+
+/* Two-batch overlap split ([LEP] "TBO": a batch is cut into two micro-batches
+ * whose stages interleave; a prefill batch at the sequence boundary whose
+ * cumulative token count is closest to half, never inside a sequence; a
+ * decode batch in half by request count).  Host code.
+ *   seq_lens  [n_seqs] host: tokens of each sequence (>= 0), in batch order
+ *   decode    nonzero: one token per request, cut at n_seqs / 2
+ * Returns i: micro-batch A is sequences [0, i), B the rest; 0 when n_seqs < 2
+ * (no cut); for prefill i minimises |2 * tokens(A) - total| over 1..n_seqs-1,
+ * ties to the lower i.  RDG_EINVAL for a negative length or count. */
+int rdg_tbo_split(const int32_t* seq_lens, int n_seqs, int decode);
 
 /* Bytes of rdg_layout.work for a dispatch of T tokens x K slots over n_local experts. */
 size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);

@@ -42,6 +42,7 @@ _SIGS = {
     "rdg_route": ([_P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "rdg_eplb_place": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "rdg_eplb_remap": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "rdg_tbo_split": ([_P, _I, _I], _I),
     "rdg_dispatch_workspace_bytes": ([_I, _I, _I], _SZ),
     "rdg_dispatch": ([_P, _P, _I, _I, _I, _P, _I, _LP, _P, _P, _P], _I),
     "rdg_layout_dense": ([_I, _LP, _P], _I),
@@ -148,6 +149,17 @@ def rdg_eplb_place(load, n_groups, n_nodes, n_gpus, n_physical, r_max):
     _check(_lib.rdg_eplb_place(hp(load), n, n_groups, n_nodes, n_gpus, n_physical, r_max, hp(phy2log), hp(log2phy),
                                hp(n_replica), hp(gpu_load)), "rdg_eplb_place")
     return phy2log, log2phy, n_replica, gpu_load
+
+
+def rdg_tbo_split(seq_lens, decode=False):
+    """Host call: seq_lens is a sequence of token counts.  Returns the number of
+    sequences in the first micro-batch."""
+    import numpy as np
+    a = np.ascontiguousarray(seq_lens, dtype=np.int32)
+    rc = _lib.rdg_tbo_split(ctypes.c_void_p(a.ctypes.data), a.shape[0], int(bool(decode)))
+    if rc < 0:
+        raise RdgError(rc, "rdg_tbo_split")
+    return rc
 
 
 def rdg_eplb_remap(ids, token_gidx, log2phy, n_replica, phys_begin, n_local, local_ids, stream=None):

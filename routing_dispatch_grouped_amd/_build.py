@@ -12,7 +12,7 @@ OUT = os.path.join(PKG, "librdg.so")
 BUILD = os.path.join(PKG, "_build")
 
 SOURCES = ["abi.hip", "route.hip", "dispatch.hip", "quant.hip", "pack.hip", "ffn.hip", "ffn_tiled.hip", "combine.hip",
-           "eplb.cpp"]
+           "eplb.cpp", "tbo.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -46,9 +46,11 @@ WORKLOADS = {
     "decode_bf16": dict(wid=2, B=128, H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048, shared_I=2048,
                         dtype="bf16", layout="masked", m_max=256, scale=1.0, logits="normal_bias"),
     "prefill_bf16": dict(wid=3, B=4096, H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048, shared_I=2048,
-                         dtype="bf16", layout="contiguous", scale=1.0, logits="zipf", zipf_s=1.1),
+                         dtype="bf16", layout="contiguous", scale=1.0, logits="zipf", zipf_s=1.1,
+                         seq_lens=[2048, 2048]),
     "prefill_bf16_balanced": dict(wid=6, B=4096, H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048,
-                                  shared_I=2048, dtype="bf16", layout="contiguous", scale=1.0, logits="normal"),
+                                  shared_I=2048, dtype="bf16", layout="contiguous", scale=1.0, logits="normal",
+                                  seq_lens=[2048, 2048]),
     "decode_rank_fp8": dict(wid=4, B_global=72 * 128, n_ranks=72, n_local=4, n_redundant=32, rows=1024,
                             H=7168, N=256, n_group=8, topk_group=4, K=8, I=2048, shared_I=0,
                             dtype="fp8", layout="masked", m_max=1024, scale=1.0, logits="zipf", zipf_s=1.1),
