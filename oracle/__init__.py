@@ -58,6 +58,8 @@ def lib():
         L.orc_sigmoid_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                         ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.orc_sigmoid_sweep.restype = ctypes.c_double
+        L.orc_route_biased.argtypes = [P, P, i32, i32, i32, i32, i32, f32, P, P]
+        L.orc_route_biased.restype = i32
         L.orc_route.argtypes = [P, i32, i32, i32, i32, i32, f32, P, P]
         L.orc_route.restype = i32
         L.orc_eplb_remap.argtypes = [P, P, i32, i32, P, P, i32, i32, i32, i32, P]
@@ -136,12 +138,17 @@ def sigmoid_sweep(lo_bits, hi_bits, stride):
     return worst, n.value, nm.value
 
 
-def route(logits, n_group, topk_group, K, scale=1.0):
+def route(logits, n_group, topk_group, K, scale=1.0, bias=None):
+    """bias: optional float32 [N] added to the scores for the choice only."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     B, N = logits.shape
     ids = np.empty((B, K), dtype=np.int32)
     w = np.empty((B, K), dtype=np.float32)
-    rc = lib().orc_route(_p(logits), B, N, n_group, topk_group, K, scale, _p(ids), _p(w))
+    if bias is None:
+        rc = lib().orc_route(_p(logits), B, N, n_group, topk_group, K, scale, _p(ids), _p(w))
+    else:
+        bias = np.ascontiguousarray(bias, dtype=np.float32)
+        rc = lib().orc_route_biased(_p(logits), _p(bias), B, N, n_group, topk_group, K, scale, _p(ids), _p(w))
     if rc != OK:
         raise ValueError("orc_route: invalid arguments")
     return ids, w

@@ -314,15 +314,19 @@ double orc_sigmoid_sweep(uint32_t lo_bits, uint32_t hi_bits, uint32_t stride, in
  * single score when a group has one expert); ties go to the lower index
  * everywhere; slot k holds the k-th expert in (score desc, id asc) order;
  * the weights are the selected scores renormalised to sum to `scale`.
+ * With a selection bias (a variant not on the pages: a per-expert correction
+ * added for the choice only), the group scores and the top-K use the fp32
+ * sums score + bias, and the weights still renormalise the plain scores.
  * ------------------------------------------------------------------------ */
-int orc_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
-              int32_t* ids, float* w) {
+static int route_impl(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                      float scale, int32_t* ids, float* w) {
     if (B < 0 || N <= 0 || n_group <= 0 || N % n_group != 0 || topk_group <= 0 || topk_group > n_group ||
         K <= 0 || K > topk_group * (N / n_group))
         return ORC_EINVAL;
 #pragma omp parallel
     {
         float* s = (float*)malloc(sizeof(float) * N);
+        float* sel = (float*)malloc(sizeof(float) * N);  /* the choosing score */
         float* gsc = (float*)malloc(sizeof(float) * n_group);
         char* gsel = (char*)malloc(n_group);
         char* esel = (char*)malloc(N);
@@ -331,15 +335,18 @@ int orc_route(const float* logits, int B, int N, int n_group, int topk_group, in
         for (int t = 0; t < B; ++t) {
             int e, j, r, k;
             double sum = 0.0;
-            for (e = 0; e < N; ++e) s[e] = orc_sigmoid(logits[(size_t)t * N + e]);
+            for (e = 0; e < N; ++e) {
+                s[e] = orc_sigmoid(logits[(size_t)t * N + e]);
+                sel[e] = bias ? s[e] + bias[e] : s[e];
+            }
             /* group score: top-1 + top-2 (with multiplicity) */
             for (j = 0; j < n_group; ++j) {
                 int i1 = -1, i2 = -1;
                 for (e = j * gs; e < (j + 1) * gs; ++e)
-                    if (i1 < 0 || s[e] > s[i1]) i1 = e;
+                    if (i1 < 0 || sel[e] > sel[i1]) i1 = e;
                 for (e = j * gs; e < (j + 1) * gs; ++e)
-                    if (e != i1 && (i2 < 0 || s[e] > s[i2])) i2 = e;
-                gsc[j] = i2 >= 0 ? s[i1] + s[i2] : s[i1];
+                    if (e != i1 && (i2 < 0 || sel[e] > sel[i2])) i2 = e;
+                gsc[j] = i2 >= 0 ? sel[i1] + sel[i2] : sel[i1];
                 gsel[j] = 0;
             }
             /* keep topk_group groups: largest score, lowest index on ties */
@@ -354,7 +361,7 @@ int orc_route(const float* logits, int B, int N, int n_group, int topk_group, in
             for (k = 0; k < K; ++k) {
                 int best = -1;
                 for (e = 0; e < N; ++e)
-                    if (gsel[e / gs] && !esel[e] && (best < 0 || s[e] > s[best])) best = e;
+                    if (gsel[e / gs] && !esel[e] && (best < 0 || sel[e] > sel[best])) best = e;
                 esel[best] = 1;
                 ids[(size_t)t * K + k] = best;
             }
@@ -363,11 +370,22 @@ int orc_route(const float* logits, int B, int N, int n_group, int topk_group, in
                 w[(size_t)t * K + k] = (float)((double)s[ids[(size_t)t * K + k]] / sum * (double)scale);
         }
         free(s);
+        free(sel);
         free(gsc);
         free(gsel);
         free(esel);
     }
     return ORC_OK;
+}
+
+int orc_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
+              int32_t* ids, float* w) {
+    return route_impl(logits, NULL, B, N, n_group, topk_group, K, scale, ids, w);
+}
+
+int orc_route_biased(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                     float scale, int32_t* ids, float* w) {
+    return route_impl(logits, bias, B, N, n_group, topk_group, K, scale, ids, w);
 }
 
 /* ------------------------------------------------------------------------

@@ -158,3 +158,53 @@ def test_route_rejects_bad_shapes(orc):
         orc.route(np.zeros((2, 10), np.float32), 4, 2, 2)   # 10 not divisible by 4
     with pytest.raises(ValueError):
         orc.route(np.zeros((2, 8), np.float32), 4, 1, 3)    # K > candidates
+
+
+# ---------------------------------------------------------------- selection-only bias
+# (a variant not on the pages: a per-expert correction added to the scores for
+# the choice only; the weights renormalise the plain scores)
+
+@pytest.mark.parametrize("n_group,gs,topk_group,K", _cases()[:20])
+@pytest.mark.parametrize("ties", [False, True])
+def test_biased_route_brute_force(orc, n_group, gs, topk_group, K, ties):
+    rng = np.random.default_rng([n_group, gs, topk_group, K, ties, 99])
+    B, N = 24, n_group * gs
+    if ties:
+        logits = rng.integers(-1, 2, (B, N)).astype(np.float32)
+        bias = (rng.integers(-2, 3, N) * 0.125).astype(np.float32)     # exact sums: ties survive
+    else:
+        logits = rng.standard_normal((B, N)).astype(np.float32)
+        bias = rng.normal(0.0, 0.7, N).astype(np.float32)             # negative choosing scores too
+    ids, w = orc.route(logits, n_group, topk_group, K, 1.0, bias=bias)
+    s = orc.sigmoid(logits)
+    for t in range(B):
+        sel = (s[t] + bias).astype(np.float32)                         # one fp32 rounding per expert
+        want, _ = brute_select(sel, n_group, topk_group, K)
+        assert list(ids[t]) == want, (t, logits[t])
+        # weights from the plain scores of the chosen experts
+        plain = np.array([float(s[t][e]) for e in ids[t]])
+        assert np.allclose(w[t], plain / plain.sum(), rtol=2e-7, atol=0)
+
+
+def test_zero_bias_is_the_plain_route(orc):
+    rng = np.random.default_rng(21)
+    logits = (rng.standard_normal((200, 256)) + rng.normal(0, 0.5, 256)).astype(np.float32)
+    a = orc.route(logits, 8, 4, 8)
+    b = orc.route(logits, 8, 4, 8, bias=np.zeros(256, np.float32))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_large_bias_forces_the_choice(orc):
+    # a +10 bias on experts 40..47 (all in group 1 of 8 groups of 32) outranks
+    # any sigmoid score: those 8 are chosen for every token, in the order of
+    # their plain scores, whatever the logits
+    rng = np.random.default_rng(22)
+    logits = rng.standard_normal((64, 256)).astype(np.float32) * 3
+    bias = np.zeros(256, np.float32)
+    bias[40:48] = 10.0
+    ids, w = orc.route(logits, 8, 4, 8, bias=bias)
+    s = orc.sigmoid(logits)
+    for t in range(64):
+        assert sorted(ids[t]) == list(range(40, 48))
+        sel = (s[t] + bias).astype(np.float32)
+        assert list(ids[t]) == sorted(range(40, 48), key=lambda e: (-sel[e], e))
