@@ -118,6 +118,16 @@ typedef struct rdg_layout {
 int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
               int32_t* topk_ids, float* topk_w, rdg_stream_t stream);
 
+/* The same with a selection-only bias (a variant not on the pages, as
+ * DeepSeek-style routers use: a per-expert correction that steers the choice
+ * without entering the weights).
+ *   bias  [N] fp32, finite: groups and experts are chosen by the fp32 sums
+ *         score + bias (same rules and ties); the weights renormalise the
+ *         plain scores of the chosen experts; slots are in (score + bias
+ *         desc, id asc) order. */
+int rdg_route_biased(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                     float scale, int32_t* topk_ids, float* topk_w, rdg_stream_t stream);
+
 /* EPLB logical -> physical remap ([LEP] self-test answer 3 and the EPLB
  * paragraph: 256 logical experts in 288 physical slots, popular experts
  * replicated, each copy taking a share; [H100] "EPLB").

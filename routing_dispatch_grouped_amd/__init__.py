@@ -40,6 +40,7 @@ _LP = ctypes.POINTER(rdg_layout)
 
 _SIGS = {
     "rdg_route": ([_P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
+    "rdg_route_biased": ([_P, _P, _I, _I, _I, _I, _I, _F, _P, _P, _P], _I),
     "rdg_eplb_place": ([_P, _I, _I, _I, _I, _I, _I, _P, _P, _P, _P], _I),
     "rdg_eplb_remap": ([_P, _P, _I, _I, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "rdg_tbo_split": ([_P, _I, _I], _I),
@@ -132,6 +133,12 @@ def rdg_route(logits, n_group, topk_group, K, scale, topk_ids, topk_w, stream=No
     B, N = logits.shape
     _check(_lib.rdg_route(_ptr(logits), B, N, n_group, topk_group, K, scale, _ptr(topk_ids), _ptr(topk_w),
                           _stream(stream)), "rdg_route")
+
+
+def rdg_route_biased(logits, bias, n_group, topk_group, K, scale, topk_ids, topk_w, stream=None):
+    B, N = logits.shape
+    _check(_lib.rdg_route_biased(_ptr(logits), _ptr(bias), B, N, n_group, topk_group, K, scale, _ptr(topk_ids),
+                                 _ptr(topk_w), _stream(stream)), "rdg_route_biased")
 
 
 def rdg_eplb_place(load, n_groups, n_nodes, n_gpus, n_physical, r_max):

@@ -87,13 +87,24 @@ const char* rdg_strerror(int code) {
     }
 }
 
-int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
-              int32_t* topk_ids, float* topk_w, rdg_stream_t stream) {
+static int route_impl(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                      float scale, int32_t* topk_ids, float* topk_w, rdg_stream_t stream) {
     if (B < 0 || N < 1 || N > 1024 || n_group < 1 || N % n_group != 0) return RDG_EINVAL;
     if (topk_group < 1 || topk_group > n_group || K < 1 || K > 32 || K > topk_group * (N / n_group))
         return RDG_EINVAL;
     if (B > 0 && (!logits || !topk_ids || !topk_w)) return RDG_EINVAL;
-    return hip_rc(launch_route(logits, B, N, n_group, topk_group, K, scale, topk_ids, topk_w, stream));
+    return hip_rc(launch_route(logits, bias, B, N, n_group, topk_group, K, scale, topk_ids, topk_w, stream));
+}
+
+int rdg_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
+              int32_t* topk_ids, float* topk_w, rdg_stream_t stream) {
+    return route_impl(logits, nullptr, B, N, n_group, topk_group, K, scale, topk_ids, topk_w, stream);
+}
+
+int rdg_route_biased(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                     float scale, int32_t* topk_ids, float* topk_w, rdg_stream_t stream) {
+    if (!bias) return RDG_EINVAL;
+    return route_impl(logits, bias, B, N, n_group, topk_group, K, scale, topk_ids, topk_w, stream);
 }
 
 int rdg_eplb_remap(const int32_t* ids, const int64_t* token_gidx, int T, int K, const int32_t* log2phy,

@@ -125,8 +125,8 @@ __host__ __device__ inline int bt_index(int bt) { return bt == 16 ? 0 : bt == 32
 // ---------------------------------------------------------------- launchers
 // Each returns hipSuccess or the launch error.  Arguments are validated by
 // the ABI layer before these are called.
-hipError_t launch_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
-                        int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_route(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                        float scale, int32_t* ids, float* w, hipStream_t s);
 hipError_t launch_remap(const int32_t* ids, const int64_t* gidx, int T, int K, const int32_t* log2phy,
                         const int32_t* n_rep, int r_max, int n_logical, int phys_begin, int n_local,
                         int32_t* out, hipStream_t s);

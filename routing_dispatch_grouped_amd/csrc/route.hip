@@ -8,12 +8,17 @@
 // the K weights are renormalised to sum to `scale`, and every tie goes to the
 // lower index.
 //
-// Design for CDNA4: a token's N <= 1024 scores sit in LDS (one wave's
-// private slice) and in registers (N/64 per lane, expert e on lane e % 64).
-// Group g's score is computed by lane g % 64; each of the
+// With a selection bias (a variant not on the pages: a per-expert correction
+// added for the choice only), groups and experts are chosen by the fp32 sums
+// score + bias, and the weights still renormalise the plain scores.
+//
+// Design for CDNA4: a token's N <= 1024 choosing scores sit in LDS (one
+// wave's private slice) and in registers (N/64 per lane, expert e on lane
+// e % 64).  Group g's score is computed by lane g % 64; each of the
 // topk_group + K selection rounds is one 64-lane max-reduction of a 64-bit
-// key (score bits << 32 | ~index) -- the positive fp32 scores order like
-// their bit patterns, and ~index makes the lower index win a tie.
+// key (ordered score bits << 32 | ~index) -- the fp32 bits mapped so that
+// unsigned order is numeric order, and ~index makes the lower index win a
+// tie.
 #include "rdg_internal.h"
 
 #pragma clang fp contract(off)
@@ -50,29 +55,42 @@ __device__ __forceinline__ float score_sigmoid(float xf) {
     return (float)(1.0 / (1.0 + e));
 }
 
+// fp32 -> uint32 whose unsigned order is the numeric order (negative values
+// have every bit flipped, non-negative ones the sign bit); never 0 for a
+// finite value
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+    const uint32_t u = __float_as_uint(v);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
 __device__ __forceinline__ uint64_t make_key(float score, int idx) {
-    return ((uint64_t)__float_as_uint(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
+    return ((uint64_t)ordered_bits(score) << 32) | (uint32_t)(0xffffffffu - (uint32_t)idx);
 }
 __device__ __forceinline__ int key_index(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
 
 template <int VPL>
-__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int B, int N, int n_group,
-                                               int topk_group, int K, float scale, int32_t* __restrict__ ids,
-                                               float* __restrict__ w) {
-    __shared__ float lds[4][64 * VPL];
+__global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, const float* __restrict__ bias,
+                                               int B, int N, int n_group, int topk_group, int K, float scale,
+                                               int32_t* __restrict__ ids, float* __restrict__ w) {
+    __shared__ float lds[4][64 * VPL];   // choosing scores
+    __shared__ float plain_lds[4][64 * VPL];  // plain scores (weights), with a bias
     __shared__ uint8_t gsel_lds[4][64 * VPL];
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int t = blockIdx.x * 4 + wv;
     if (t >= B) return;  // the wave is idle; nothing below synchronises across waves
     float* s_lds = lds[wv];
+    float* p_lds = plain_lds[wv];
     const float* row = logits + (size_t)t * N;
 
-    float s[VPL];
+    float s[VPL];  // choosing scores
 #pragma unroll
     for (int v = 0; v < VPL; ++v) {
         int e = lane + kWave * v;
-        s[v] = e < N ? score_sigmoid(row[e]) : 0.0f;
-        if (e < N) s_lds[e] = s[v];
+        const float plain = e < N ? score_sigmoid(row[e]) : 0.0f;
+        s[v] = bias && e < N ? plain + bias[e] : plain;
+        if (e < N) {
+            s_lds[e] = s[v];
+            if (bias) p_lds[e] = plain;
+        }
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
@@ -87,7 +105,7 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
         const int g = lane + kWave * j;
         gkey[j] = 0ull;
         if (g < n_group) {
-            float a = -1.0f, b = -1.0f;
+            float a = -__builtin_inff(), b = -__builtin_inff();
             for (int i = g * gs; i < (g + 1) * gs; ++i) {
                 const float v = s_lds[i];
                 if (v > a) {
@@ -135,12 +153,11 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 #pragma unroll
         for (int v = 0; v < VPL; ++v)
             if (lane + kWave * v == e) key[v] = 0ull;
-        if (lane == k) {
-            my_id = e;
-            my_s = __uint_as_float((uint32_t)(m >> 32));
-        }
+        if (lane == k) my_id = e;
     }
-    // renormalise: fp32 sum in slot order, then w_k = s_k / sum * scale
+    // renormalise the plain scores: fp32 sum in slot order, then
+    // w_k = s_k / sum * scale
+    if (lane < K) my_s = bias ? p_lds[my_id] : s_lds[my_id];
     float sum = 0.0f;
     for (int k = 0; k < K; ++k) sum += __shfl(my_s, k);
     if (lane < K) {
@@ -151,16 +168,16 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 
 }  // namespace
 
-hipError_t launch_route(const float* logits, int B, int N, int n_group, int topk_group, int K, float scale,
-                        int32_t* ids, float* w, hipStream_t s) {
+hipError_t launch_route(const float* logits, const float* bias, int B, int N, int n_group, int topk_group, int K,
+                        float scale, int32_t* ids, float* w, hipStream_t s) {
     if (B == 0) return hipSuccess;
     dim3 grid((B + 3) / 4), block(256);
     if (N <= 64)
-        k_route<1><<<grid, block, 0, s>>>(logits, B, N, n_group, topk_group, K, scale, ids, w);
+        k_route<1><<<grid, block, 0, s>>>(logits, bias, B, N, n_group, topk_group, K, scale, ids, w);
     else if (N <= 256)
-        k_route<4><<<grid, block, 0, s>>>(logits, B, N, n_group, topk_group, K, scale, ids, w);
+        k_route<4><<<grid, block, 0, s>>>(logits, bias, B, N, n_group, topk_group, K, scale, ids, w);
     else
-        k_route<16><<<grid, block, 0, s>>>(logits, B, N, n_group, topk_group, K, scale, ids, w);
+        k_route<16><<<grid, block, 0, s>>>(logits, bias, B, N, n_group, topk_group, K, scale, ids, w);
     return hipGetLastError();
 }
 

@@ -67,3 +67,31 @@ def test_route_empty_batch():
     m.rdg_route(torch.zeros((0, 256), device=DEV), 8, 4, 8, 1.0, ids, w)
     torch.cuda.synchronize()
     assert int(ids.abs().sum()) == 0
+
+
+# selection-only bias (a variant not on the pages): ids bit-exact, weights from
+# the plain scores to the same rounding bound
+@pytest.mark.parametrize("B,N,n_group,topk_group,K,std", [
+    (4096, 256, 8, 4, 8, 0.5), (333, 256, 8, 4, 8, 3.0), (77, 16, 4, 2, 4, 0.3), (50, 1024, 64, 8, 32, 0.2),
+    (300, 96, 12, 5, 7, 1.0)])
+def test_route_biased(B, N, n_group, topk_group, K, std):
+    m = rdg()
+    rng = np.random.default_rng([B, N, 5])
+    for ties in (False, True):
+        if ties:
+            logits = rng.integers(-1, 2, (B, N)).astype(np.float32)
+            bias = (rng.integers(-2, 3, N) * 0.125).astype(np.float32)
+        else:
+            logits = rng.standard_normal((B, N)).astype(np.float32)
+            bias = rng.normal(0.0, std, N).astype(np.float32)
+        ids = torch.full((B, K), -7, dtype=torch.int32, device=DEV)
+        w = torch.zeros((B, K), dtype=torch.float32, device=DEV)
+        m.rdg_route_biased(torch.from_numpy(logits).to(DEV), torch.from_numpy(bias).to(DEV), n_group, topk_group, K,
+                           1.0, ids, w)
+        gi, gw = np_of(ids), np_of(w)
+        ri, rw = oracle.route(logits, n_group, topk_group, K, 1.0, bias=bias)
+        bad = np.flatnonzero((gi != ri).any(1))
+        print("biased route", B, N, n_group, topk_group, K, std, ties, "differing tokens", len(bad), flush=True)
+        assert len(bad) == 0, (bad[:10], gi[bad[:3]], ri[bad[:3]])
+        bound = (K + 2) * 2.0 ** -24
+        assert np.max(np.abs(gw.astype(np.float64) - rw) / np.maximum(np.abs(rw), 1e-30)) <= bound
