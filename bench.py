@@ -56,10 +56,11 @@ def parse():
     return p.parse_args()
 
 
-# Files whose contents determine the dominant kernel's memory traffic; the
-# committed counter figures apply only while their hash is unchanged.
+# Files whose contents determine the dominant kernel's memory traffic (the
+# kernel, its device helpers and the packed weight layout); the committed
+# counter figures apply only while their hash is unchanged.
 TRAFFIC_SOURCES = ["routing_dispatch_grouped_amd/csrc/ffn.hip", "routing_dispatch_grouped_amd/csrc/rdg_internal.h",
-                   "routing_dispatch_grouped_amd/csrc/pack.hip", "routing_dispatch_grouped_amd/csrc/abi.hip"]
+                   "routing_dispatch_grouped_amd/csrc/pack.hip"]
 
 
 def source_hash():
