@@ -209,6 +209,23 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
     row = check_rows(got, ref, cfg, cfg["name"])
     print("%s worst token relative error %.3e" % (cfg["name"], row), flush=True)
     assert err <= tolerance(cfg), err
+    # for information: the error of the whole fp8 path (quantised x, W and h)
+    # against the layer computed in fp64 from the unquantised weights and the
+    # bf16 tokens, on 8 of the sampled tokens
+    few = sel[:8]
+    xb = np_of(x_bf)
+    ref_u = np.zeros((len(few), cfg["H"]))
+    for j, e in enumerate(share["local_logical"]):
+        wt = synth.expert_weights(cfg, e, device=DEV)
+        W1, W3, W2 = (wt[k].double().cpu().numpy() for k in ("W1", "W3", "W2"))
+        for i, t in enumerate(few):
+            for k in range(rloc.shape[1]):
+                if rloc[t, k] == j:
+                    a = oracle.bf16_decode(xb[t])
+                    g, u = W1 @ a, W3 @ a
+                    ref_u[i] += float(share["w"][t, k]) * (W2 @ (g / (1.0 + np.exp(-g)) * u))
+    err_u = oracle.rel_err(out_as_f64(got[:len(few)]), ref_u)
+    print("%s error against the unquantised fp64 layer (information) %.3e" % (cfg["name"], err_u), flush=True)
     return r, share, experts, (xq, x_s, loc, rloc, rq, rs, oe)
 
 
