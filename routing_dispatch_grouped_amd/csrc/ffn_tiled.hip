@@ -19,19 +19,21 @@
 // tiles are consecutive rows of W2 (output columns).
 //
 // The reduction dimension is walked in chunks of CB bytes per row.  The
-// token tile is shared by the eight waves, so its chunks go through a
-// two-slot LDS ring filled by direct global->LDS loads; each 16-byte piece is
-// stored at a row-dependent XOR of its index (chosen through each lane's
+// token tile is shared by the eight waves, so its chunks go through an LDS
+// ring of NSLOT slots filled by direct global->LDS loads; each 16-byte piece
+// is stored at a row-dependent XOR of its index (chosen through each lane's
 // source address) that makes the MFMA-layout LDS reads conflict-free.  Weight
 // operand tiles are private to a wave and arrive packed (pack.hip: one
-// contiguous KiB per load instruction) straight into one of two register
+// contiguous KiB per load instruction) straight into one of NSLOT register
 // sets; a weight panel is re-read by every row tile of its expert, mostly
-// from L2.  While chunk k is multiplied, chunk k+1's token rows (into the
-// other ring slot) and weights (into the other register set) are in flight;
-// the loop is unrolled by two so that slots and register sets are named at
-// compile time (no register copies that would wait for a load in flight, and
-// the compiler can tell the slots apart), with one wait and one barrier per
-// chunk.
+// from L2.  While chunk k is multiplied, the next NSLOT-1 chunks' token rows
+// and weights are in flight (bf16: three slots of 64 bytes per row, which
+// keeps twice as many bytes in flight per CU as two slots of 128 for the
+// same registers; fp8: two slots, whose larger chunks halve the barriers of
+// its LDS-bound loop); the loop is unrolled by NSLOT so that slots and
+// register sets are named at compile time (no register copies that would
+// wait for a load in flight, and the compiler can tell the slots apart),
+// with one wait and one barrier per chunk.
 // fp8 tiles also stage each chunk's activation scales (two 1x128 blocks per
 // row) through the ring; every 128-long block's MFMA partial is promoted into
 // the fp32 accumulator with its activation and weight scales.
@@ -62,10 +64,12 @@ struct TOp;
 // One MFMA operand read touches one piece of 16 consecutive rows; the XOR
 // puts those 16 pieces in distinct 16-byte bank groups (rows of 256 bytes or
 // more: by r % 16; rows of 128 bytes, two to a 256-byte bank cycle: by
-// (r / 2) % 8).  An involution, so it also maps slots back to pieces.
+// (r / 2) % 8; rows of 64 bytes, four to a cycle: by (r / 4) % 4).  An
+// involution, so it also maps slots back to pieces.
 template <int CB>
 __device__ __forceinline__ int piece_slot(int r, int c) {
-    return CB >= 256 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+    static_assert(CB == 64 || CB == 128 || CB % 256 == 0, "chunk of 64, 128 or a multiple of 256 bytes per row");
+    return CB >= 256 ? (c ^ (r & 15)) : CB == 128 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
 // Per type: the MFMA step KS (reduction elements), element size, the packed
@@ -137,9 +141,10 @@ struct TOp<RDG_FP8_E4M3> {
     }
 };
 
-// Tile shape: NRT 16-row weight tiles per wave and the chunk CB (bytes of
-// each row per chunk), sized so that two chunks of weights in registers, the
-// accumulators and the operand pipeline fit two waves per SIMD.  WIDE: 64
+// Tile shape: NRT 16-row weight tiles per wave, the chunk CB (bytes of each
+// row per chunk) and the ring depth NSLOT, sized so that NSLOT chunks of
+// weights in registers, the accumulators and the operand pipeline fit two
+// waves per SIMD.  WIDE: 64
 // weight rows per wave, so each token operand read from LDS feeds four MFMAs
 // (bf16, and fp8 with power-of-two scales when the grid still fills the
 // chip); otherwise 32 rows (fp8 with fp32 scales keeps registers for the
@@ -148,15 +153,15 @@ template <int DT, bool WIDE>
 struct TShape;
 template <>
 struct TShape<RDG_BF16, true> {
-    static constexpr int NRT = 4, CB = 128;
+    static constexpr int NRT = 4, CB = 64, NSLOT = 3;
 };
 template <>
 struct TShape<RDG_FP8_E4M3, false> {
-    static constexpr int NRT = 2, CB = 256;
+    static constexpr int NRT = 2, CB = 256, NSLOT = 2;
 };
 template <>
 struct TShape<RDG_FP8_E4M3, true> {
-    static constexpr int NRT = 4, CB = 128;
+    static constexpr int NRT = 4, CB = 128, NSLOT = 2;
 };
 
 template <int DT, bool WIDE>
@@ -225,7 +230,7 @@ __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int 
         const uint8_t* src = a.X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
         __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(ring.x + q * 1024), 16, 0, 0);
     }
-    if (DT == RDG_FP8_E4M3) {
+    if constexpr (DT == RDG_FP8_E4M3) {
         // lanes 0..16*SPB-1 of wave w: row 16w + l/SPB, scale block SPB*kc + l%SPB
         static_assert(TB == 16 * NW && SPB * 16 <= 64, "one load of scales per wave");
         const int l = lane % (16 * SPB);
@@ -251,14 +256,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     constexpr int NOT = GATED ? NRT / 2 : NRT;       // 16-column output tiles per wave
     constexpr bool FP8 = DT == RDG_FP8_E4M3;
     constexpr int CHUNK_LDS = TB * CB, SPB = CB / 128;
+    constexpr int NSLOT = TShape<DT, WIDE>::NSLOT;
+    static_assert(NSLOT == 2 || (NSLOT == 3 && !FP8), "two slots, or three without scale slots");
     static_assert(!GATED || NRT % 2 == 0, "a gated wave holds its W1 and W3 tiles in pairs");
     __shared__ __attribute__((aligned(16))) uint8_t lx0[CHUNK_LDS];
     __shared__ __attribute__((aligned(16))) uint8_t lx1[CHUNK_LDS];
+    __shared__ __attribute__((aligned(16))) uint8_t lx2[NSLOT > 2 ? CHUNK_LDS : 16];
     __shared__ __attribute__((aligned(16))) float ls0[FP8 ? TB * SPB : 4];
     __shared__ __attribute__((aligned(16))) float ls1[FP8 ? TB * SPB : 4];
     __shared__ __attribute__((aligned(16))) float lw0[FP8 ? NW * 2 * S : 4];
     __shared__ __attribute__((aligned(16))) float lw1[FP8 ? NW * 2 * S : 4];
-    const Ring ring[2] = {{lx0, ls0, lw0}, {lx1, ls1, lw1}};
+    const Ring ring[3] = {{lx0, ls0, lw0}, {lx1, ls1, lw1}, {lx2, ls0, lw0}};
 
     int fb, tile;
     if (SIGNAL) {
@@ -332,7 +340,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // weight block scales travel with the token chunk's ring slot (direct
     // loads into LDS: a register load of them would make the compiler wait
     // for the chunk in flight to copy it)
-    op_t w[2][S][NRT];
+    op_t w[NSLOT][S][NRT];
 
     auto request_w = [&](int kc, op_t (&wr)[S][NRT], const Ring& rg) {
         O::template load_w<S, NRT>(wr, wt, kc * S, lane);
@@ -413,11 +421,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         if (FP8 && !PW2) promote(NI - 1);
     };
 
-    // Chunk k+1's token rows and weights are requested once chunk k has
-    // arrived, and are in flight while chunk k is multiplied.  A tile with
-    // fewer valid rows (an expert's last tile) only stages and multiplies
-    // the 16-row token tiles that hold them: wave w stages rows [16w, 16w+16).
-    auto main_loop = [&](auto nv) {
+    // Two slots: chunk k+1's token rows and weights are requested once chunk
+    // k has arrived, and are in flight while chunk k is multiplied.  A tile
+    // with fewer valid rows (an expert's last tile) only stages and
+    // multiplies the 16-row token tiles that hold them: wave w stages rows
+    // [16w, 16w+16).
+    auto main_loop2 = [&](auto nv) {
         constexpr int NV = decltype(nv)::value;
         if (wv < NV) stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
         request_w(0, w[0], ring[0]);
@@ -439,6 +448,41 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 compute(ring[j], w[j], nv);
             }
         }
+    };
+    // Three slots: chunk k+2 is requested while chunk k is multiplied, so
+    // chunk k+1's loads stay in flight across the wait for chunk k.  Every
+    // wave issues the same LPC loads for every chunk (all rows of the tile,
+    // the clamped ones re-reading the last valid row; past the last chunk it
+    // re-reads that chunk into the free slot), so that one count, "at most
+    // LPC loads outstanding", means chunk k has landed.  Every slot of an
+    // iteration issues its loads and the loop exits only at its latch: the
+    // compiler's own wait counts stay exact (an early exit would make it
+    // assume the latest loads may still write the next iteration's first
+    // register set).  The last loads are drained before the epilogue.
+    auto main_loop3 = [&](auto nv) {
+        constexpr int LPC = TB * CB / 1024 / NW + S * NRT;  // vector-memory loads per chunk and wave
+        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+        request_w(0, w[0], ring[0]);
+        const int c1 = nchunks > 1 ? 1 : 0;
+        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, c1, ring[1], wv, lane);
+        request_w(c1, w[1], ring[1]);
+        for (int kc0 = 0; kc0 < nchunks; kc0 += 3) {
+#pragma unroll
+            for (int j = 0; j < 3; ++j) {
+                const int kc = kc0 + j;
+                __builtin_amdgcn_s_waitcnt(vmcnt_imm<LPC>());
+                lds_barrier();
+                const int kn = kc + 2 < nchunks ? kc + 2 : nchunks - 1;
+                stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, kn, ring[(j + 2) % 3], wv, lane);
+                request_w(kn, w[(j + 2) % 3], ring[(j + 2) % 3]);
+                if (kc < nchunks) compute(ring[j], w[j], nv);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm<0>());
+    };
+    auto main_loop = [&](auto nv) {
+        if constexpr (NSLOT == 3) main_loop3(nv);
+        else main_loop2(nv);
     };
     // (fp8: the full tile only -- a second copy of the loop does not fit its
     // registers)
