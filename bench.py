@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--tbo", action="store_true",
                    help="prefill layers as two micro-batches cut at a sequence boundary, on two streams "
                         "(the roofline then covers micro-batch A's gate/up)")
-    p.add_argument("--cpu-tokens", type=int, default=16, help="tokens in the CPU-oracle sample (0: skip)")
+    p.add_argument("--cpu-tokens", type=int, default=-1,
+                   help="tokens in the CPU-oracle sample (-1: the whole batch; 0: skip)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
                         "size, for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiling run)")
@@ -471,8 +472,9 @@ def main():
     line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof}
-    if args.cpu_tokens > 0 and not b.rank and args.workload == "decode_bf16":
-        line["cpu_baseline"] = cpu_baseline(b, args.cpu_tokens)
+    if args.cpu_tokens != 0 and not b.rank and args.workload == "decode_bf16":
+        n_tok = b.logits_np.shape[0] if args.cpu_tokens < 0 else min(args.cpu_tokens, b.logits_np.shape[0])
+        line["cpu_baseline"] = cpu_baseline(b, n_tok)
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -484,9 +486,9 @@ def main():
 
 
 def cpu_baseline(b, n_tok):
-    """The CPU oracle, as it stands, on a bounded sample of the same workload:
-    routing of the whole batch, the layout, and the layer output of the first
-    n_tok tokens.  Host copies of the needed inputs (from the generator) are
+    """The CPU oracle, as it stands, on the same workload: routing of the whole
+    batch, the layout, and the layer output of the first n_tok tokens (by
+    default all of them: about 8 s on 16 cores).  Host copies of the needed inputs (from the generator) are
     made before the clock starts."""
     import numpy as np
     import torch
@@ -511,8 +513,10 @@ def cpu_baseline(b, n_tok):
     dt = time.perf_counter() - t0
     return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "seconds": dt,
-            "sample": "route all %d tokens, layout, and the fp64 layer output (8 routed experts + shared) of "
-                      "the first %d tokens" % (b.logits_np.shape[0], n_tok)}
+            "sample": ("the whole batch: routing, layout and the fp64 layer output (8 routed experts + shared) "
+                       "of all %d tokens" % n_tok) if n_tok == b.logits_np.shape[0] else
+                      ("route all %d tokens, layout, and the fp64 layer output (8 routed experts + shared) of "
+                       "the first %d tokens" % (b.logits_np.shape[0], n_tok))}
 
 
 if __name__ == "__main__":
