@@ -380,8 +380,8 @@ class Bench:
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU's share of the layer; multi-GPU runs (--gpus %d) are not part of this "
-              "build (the expert-parallel sharding is described, not implemented)" % args.gpus, file=sys.stderr)
+        print("bench.py measures one GPU's share of the layer; runs on several GPUs (--gpus %d) are not "
+              "supported (the expert-parallel sharding is described, not implemented)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
