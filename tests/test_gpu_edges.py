@@ -137,3 +137,25 @@ def test_fp8u_wide_panels(kind):
     ref = oracle.moe_layer(dt_code(cfg), xo, ids_np, w_np, [experts.oracle_expert(e) for e in range(2)],
                            x_scales=xo_s, sel=sel)
     _compare(cfg, np_of(r["out"])[sel], ref, "fp8u wide kind=%d" % kind)
+
+
+@pytest.mark.parametrize("H,I", [(1536, 768), (1024, 512), (512, 768)])
+def test_tiled_bf16_chunk_counts(H, I):
+    """bf16 through the 128-row kernels (64-byte chunks, three ring slots) for
+    reduction lengths whose chunk counts leave each remainder modulo three
+    (gate/up / down: 48 / 24, 32 / 16, 16 / 24 chunks), with ragged experts;
+    every output row against the oracle."""
+    m = rdg()
+    cfg = dict(_cfg("bf16", H=H, I=I, N=4, K=2, wid=750 + H + I), n_group=2, topk_group=1)
+    T = 300
+    logits = synth.logits(cfg, T)
+    ri, rw = oracle.route(logits, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ri).to(DEV), torch.from_numpy(rw).to(DEV), experts,
+                   m.RDG_CONTIGUOUS, block_m=128)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    assert m.rdg_signal_rows(r["L"], m.RDG_BF16, H, I) == 128  # the row tile the FFN ran with
+    ref = oracle.moe_layer(dt_code(cfg), xo, ri, rw, [experts.oracle_expert(j) for j in range(cfg["N"])],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "tiled bf16 H=%d I=%d" % (H, I))
