@@ -24,6 +24,8 @@
 // partial sum is promoted into the fp32 accumulator with its activation and
 // weight block scales).  The row-tile -> expert mapping comes from the prefix
 // table the dispatch built, so no host sync is needed for dynamic shapes.
+#include <type_traits>
+
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -336,9 +338,11 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
 // consecutive workgroups, which stream neighbouring weight panels of one
 // expert and share its token rows in L2 (and signalled row tiles complete in
 // layout order).  Many short workgroups instead of few long ones keep the
-// last round of the grid from idling most of the GPU.  With NR = 1 an expert's weights are read once per
-// 16-row tile and are streamed past the caches; with NR > 1 the row groups of
-// one weight panel re-read it, so the loads stay cacheable.  Used for every
+// last round of the grid from idling most of the GPU.  An expert's weights
+// are read once per row tile: streamed past the caches when its rows fit one
+// tile; when they span several (NR > 1, or a busy expert of a decode batch),
+// the loads stay cacheable, and the sibling tiles -- consecutive rows of the
+// grid, so on the same XCD at about the same time -- find them in L2.  Used for every
 // type except the fp8 gate/up stage, whose 1x128 re-quantisation of h needs
 // 128 columns in one workgroup.
 template <int DT, bool GATED, bool SIGNAL, int FPW, int NR>
@@ -392,7 +396,10 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         xv[nr] = xr[nr] < row_end;
         xrow[nr] = a.X + (size_t)(xv[nr] ? xr[nr] : row0) * wstride;
     }
-    auto wload = [&](const uint8_t* t) { return NR == 1 ? M::load_tile(t, lane) : M::load_tile_cached(t, lane); };
+    // weights of an expert whose rows span several row tiles are read by
+    // each of them: then cacheable loads, so that the sibling tiles (run
+    // side by side on the same XCD) find them in L2; otherwise streamed
+    const bool shared_panel = NR > 1 || a.masked_m[e] > BT;
 
     f32x4_t accA[FPW][NR], accB[FPW][NR];
 #pragma unroll
@@ -409,53 +416,61 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
         was = a.Was + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
         if (GATED) wbs = a.Wbs + ((size_t)e * (a.Nout / 128) + f0 / 128) * nkb;
     }
-    for (int kb = wv; kb < nkb; kb += 4) {
-        if (DT != RDG_FP8_E4M3) {
+    auto kloop = [&](auto cached) {
+        auto wload = [&](const uint8_t* t) {
+            if constexpr (decltype(cached)::value) return M::load_tile_cached(t, lane);
+            else return M::load_tile(t, lane);
+        };
+        for (int kb = wv; kb < nkb; kb += 4) {
+            if (DT != RDG_FP8_E4M3) {
 #pragma unroll
-            for (int k0 = kb * 128; k0 < kb * 128 + 128; k0 += KS * U) {
-                op_t ra[U][FPW], rb[U][FPW], rx[U][NR];
+                for (int k0 = kb * 128; k0 < kb * 128 + 128; k0 += KS * U) {
+                    op_t ra[U][FPW], rb[U][FPW], rx[U][NR];
 #pragma unroll
-                for (int u = 0; u < U; ++u) {
+                    for (int u = 0; u < U; ++u) {
 #pragma unroll
-                    for (int rt = 0; rt < FPW; ++rt) {
-                        const size_t t_off = (size_t)(k0 / KS + u) * M::BLK;
-                        ra[u][rt] = wload(arow[rt] + t_off);
-                        if (GATED) rb[u][rt] = wload(brow[rt] + t_off);
+                        for (int rt = 0; rt < FPW; ++rt) {
+                            const size_t t_off = (size_t)(k0 / KS + u) * M::BLK;
+                            ra[u][rt] = wload(arow[rt] + t_off);
+                            if (GATED) rb[u][rt] = wload(brow[rt] + t_off);
+                        }
+#pragma unroll
+                        for (int nr = 0; nr < NR; ++nr) rx[u][nr] = xv[nr] ? M::load(xrow[nr], k0 + u * KS, lane) : M::zero();
                     }
 #pragma unroll
-                    for (int nr = 0; nr < NR; ++nr) rx[u][nr] = xv[nr] ? M::load(xrow[nr], k0 + u * KS, lane) : M::zero();
+                    for (int u = 0; u < U; ++u)
+#pragma unroll
+                        for (int rt = 0; rt < FPW; ++rt)
+#pragma unroll
+                            for (int nr = 0; nr < NR; ++nr) {
+                                accA[rt][nr] = M::mma(accA[rt][nr], ra[u][rt], rx[u][nr]);
+                                if (GATED) accB[rt][nr] = M::mma(accB[rt][nr], rb[u][rt], rx[u][nr]);
+                            }
                 }
-#pragma unroll
-                for (int u = 0; u < U; ++u)
-#pragma unroll
-                    for (int rt = 0; rt < FPW; ++rt)
-#pragma unroll
-                        for (int nr = 0; nr < NR; ++nr) {
-                            accA[rt][nr] = M::mma(accA[rt][nr], ra[u][rt], rx[u][nr]);
-                            if (GATED) accB[rt][nr] = M::mma(accB[rt][nr], rb[u][rt], rx[u][nr]);
-                        }
-            }
-        } else {
-            op_t ra[FPW], rb[FPW];
-#pragma unroll
-            for (int rt = 0; rt < FPW; ++rt) {
-                ra[rt] = wload(arow[rt] + (size_t)kb * M::BLK);
-                if (GATED) rb[rt] = wload(brow[rt] + (size_t)kb * M::BLK);
-            }
-            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int nr = 0; nr < NR; ++nr) {
-                const op_t rx = xv[nr] ? M::load(xrow[nr], kb * 128, lane) : M::zero();
-                const float sx = xv[nr] ? a.Xs[(size_t)xr[nr] * nkb + kb] : 0.0f;
-                const float fa = sx * was[kb], fb = GATED ? sx * wbs[kb] : 0.0f;
+            } else {
+                op_t ra[FPW], rb[FPW];
 #pragma unroll
                 for (int rt = 0; rt < FPW; ++rt) {
-                    accA[rt][nr] += M::mma(z, ra[rt], rx) * fa;
-                    if (GATED) accB[rt][nr] += M::mma(z, rb[rt], rx) * fb;
+                    ra[rt] = wload(arow[rt] + (size_t)kb * M::BLK);
+                    if (GATED) rb[rt] = wload(brow[rt] + (size_t)kb * M::BLK);
+                }
+                const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int nr = 0; nr < NR; ++nr) {
+                    const op_t rx = xv[nr] ? M::load(xrow[nr], kb * 128, lane) : M::zero();
+                    const float sx = xv[nr] ? a.Xs[(size_t)xr[nr] * nkb + kb] : 0.0f;
+                    const float fa = sx * was[kb], fb = GATED ? sx * wbs[kb] : 0.0f;
+#pragma unroll
+                    for (int rt = 0; rt < FPW; ++rt) {
+                        accA[rt][nr] += M::mma(z, ra[rt], rx) * fa;
+                        if (GATED) accB[rt][nr] += M::mma(z, rb[rt], rx) * fb;
+                    }
                 }
             }
         }
-    }
+    };
+    if (shared_panel) kloop(std::true_type{});
+    else kloop(std::false_type{});
     // reduce the four K ranges in wave order
 #pragma unroll
     for (int rt = 0; rt < FPW; ++rt)
