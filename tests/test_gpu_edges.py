@@ -159,3 +159,33 @@ def test_tiled_bf16_chunk_counts(H, I):
     ref = oracle.moe_layer(dt_code(cfg), xo, ri, rw, [experts.oracle_expert(j) for j in range(cfg["N"])],
                            x_scales=xo_s)
     _compare(cfg, np_of(r["out"]), ref, "tiled bf16 H=%d I=%d" % (H, I))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
+@pytest.mark.parametrize("kind", [0, 1])
+def test_weight_streaming_experts_over_several_tiles(dtype, kind):
+    """16-row tiles of the weight-streaming kernels (15 rows per expert on
+    average) where experts 0 and 3 hold 40 and 20 rows: their second and third
+    tiles read the same weights (cacheable loads, shared in L2), the others
+    stream theirs; every output row against the oracle."""
+    m = rdg()
+    cfg = _cfg(dtype, H=512, I=256, N=16, K=2, wid=770)
+    T = 120
+    rng = np.random.default_rng(11)
+    first = np.concatenate([np.zeros(40, np.int32), np.full(20, 3, np.int32),
+                            rng.choice([1, 2] + list(range(4, 16)), size=T - 60).astype(np.int32)])
+    ids_np = np.stack([first, (first + 1 + rng.integers(0, 14, T)) % 16], 1).astype(np.int32)
+    ids_np[ids_np[:, 1] == ids_np[:, 0], 1] = (ids_np[ids_np[:, 1] == ids_np[:, 0], 0] + 5) % 16
+    counts = np.bincount(ids_np.ravel(), minlength=16)
+    assert counts[0] >= 40 and counts[3] >= 20 and counts.sum() == 2 * T
+    w_np = rng.uniform(0.2, 0.8, size=(T, 2)).astype(np.float32)
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    m_max = 64 if kind == m.RDG_MASKED else 0
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ids_np).to(DEV), torch.from_numpy(w_np).to(DEV), experts, kind,
+                   block_m=16, m_max=m_max)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    assert m.rdg_signal_rows(r["L"], dt_code(cfg), cfg["H"], cfg["I"]) == 16  # 16-row tiles
+    ref = oracle.moe_layer(dt_code(cfg), xo, ids_np, w_np, [experts.oracle_expert(j) for j in range(cfg["N"])],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "experts over several tiles %s kind=%d" % (dtype, kind))
