@@ -124,6 +124,7 @@ class Bench:
             self._setup_full()
             if tbo:
                 self._setup_tbo()
+        self._setup_rotation()
 
     # ------------------------------------------------------------ weights
     def _experts(self, ids, shared=False):
@@ -150,6 +151,29 @@ class Bench:
                 rdg.rdg_pack_weights(src, self.DT, W[k][j])
             del w
         return W, S
+
+    def _setup_rotation(self):
+        """Weights that fit the 256 MB last-level cache would be served from it
+        by the next step: such workloads get copies of their expert weights
+        (at least four, together at least 1 GiB), used in turn, one per step,
+        so that every step reads its weights from HBM."""
+        torch = self.torch
+        sets = [(self.W, self.S, getattr(self, "Wsh", {}), getattr(self, "Ssh", {}))]
+        nbytes = sum(t.numel() * t.element_size() for d in sets[0] for t in d.values())
+        n_sets = 1
+        if nbytes < (1 << 30):
+            n_sets = max(4, -(-(1 << 30) // nbytes))
+        for _ in range(n_sets - 1):
+            sets.append(tuple({k: v.clone() for k, v in d.items()} for d in sets[0]))
+        torch.cuda.synchronize()
+        self.weight_sets, self.weight_set_bytes, self.step_index = sets, nbytes, 0
+
+    def _next_weights(self):
+        sets = self.weight_sets
+        self.W, self.S, Wsh, Ssh = sets[self.step_index % len(sets)]
+        if Wsh:
+            self.Wsh, self.Ssh = Wsh, Ssh
+        self.step_index += 1
 
     def _quant(self, x):
         torch, rdg = self.torch, self.rdg
@@ -329,6 +353,7 @@ class Bench:
     def step(self, timed=False):
         rdg, cfg = self.rdg, self.cfg
         H, I, K = cfg["H"], cfg["I"], cfg["K"]
+        self._next_weights()
         if self.tbo:
             return self._step_tbo(timed)
         if not self.rank:
@@ -460,7 +485,8 @@ def main():
     conf = {"workload": args.workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
-            "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph)}
+            "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph),
+            "weight_sets": len(b.weight_sets)}
     if b.tbo:
         conf["tbo_micro_batches"] = [mb["T"] for mb in b.tbo]
     if b.fp8:
