@@ -92,6 +92,30 @@ def measured_traffic(workload):
         return None
 
 
+def layer_bytes(cfg, T, R, A, esz):
+    """Algorithmic HBM bytes of one whole step (every kernel's reads and
+    writes counted once: no padding, no unused masked capacity): routing (or,
+    for a rank's share, the replica remap), the stable ranks and the row
+    permutation, the routed gate/up and down GEMMs, the shared expert where
+    there is one, and the combine.  fp8 block scales are 4-byte floats."""
+    H, I, K, N = cfg["H"], cfg["I"], cfg["K"], cfg["N"]
+    ysz = 4 if cfg["dtype"] == "f32" else 2
+    sc = 4 if cfg["dtype"] == "fp8" else 0
+    rank = "B_global" in cfg
+    shI = cfg.get("shared_I", 0)
+    Tsh = cfg.get("own_tokens", T) if rank else T
+    b = T * K * 8 + T * 8 if rank else T * N * 4 + T * K * 8            # remap / route
+    b += T * K * 8                                                       # stable ranks
+    b += T * H * esz + R * H * esz + (T + R) * (H // 128) * sc           # permute rows
+    b += A * 2 * I * H * esz + A * 2 * (I // 128) * (H // 128) * sc + R * (H + I) * esz + R * (H + I) // 128 * sc
+    b += A * I * H * esz + A * (I // 128) * (H // 128) * sc + R * (I * esz + H * ysz) + R * (I // 128) * sc
+    if shI:
+        b += 3 * shI * H * esz + 3 * (shI // 128) * (H // 128) * sc + Tsh * (2 * H + 2 * shI) * esz
+        b += Tsh * H * (ysz - esz)
+    b += R * H * ysz + T * H * ysz + (T * H * ysz if (shI and not rank) else 0)  # combine
+    return b
+
+
 class Bench:
     """Buffers and the step of one workload."""
 
@@ -495,9 +519,13 @@ def main():
         conf["m_max"] = cfg["m_max"]
     if b.rank:
         conf.update(local_experts=cfg["n_local"], ranks=cfg["n_ranks"], received_rows=rows)
+    # the whole step against HBM: every kernel's algorithmic bytes over the step time
+    lb = layer_bytes(cfg, b.T, rows, active, esz)
+    layer = {"algorithmic_bytes": lb, "achieved": lb / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof}
+            "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof, "layer": layer}
     if args.cpu_tokens != 0 and not b.rank and args.workload == "decode_bf16":
         n_tok = b.logits_np.shape[0] if args.cpu_tokens < 0 else min(args.cpu_tokens, b.logits_np.shape[0])
         line["cpu_baseline"] = cpu_baseline(b, n_tok)
