@@ -61,15 +61,22 @@ template <int DT>
 struct TOp;
 
 // LDS slot of 16-byte piece c of tile row r in a chunk of CB bytes per row.
-// One MFMA operand read touches one piece of 16 consecutive rows; the XOR
-// puts those 16 pieces in distinct 16-byte bank groups (rows of 256 bytes or
-// more: by r % 16; rows of 128 bytes, two to a 256-byte bank cycle: by
-// (r / 2) % 8; rows of 64 bytes, four to a cycle: by (r / 4) % 4).  An
-// involution, so it also maps slots back to pieces.
+// One MFMA operand read touches one piece of 16 consecutive rows, and the
+// XOR spreads those pieces over the LDS banks.  Rows of 256 bytes or more:
+// by r % 16, conflict-free.  Rows of 128 bytes (the wide fp8 tile): by r % 8,
+// flipped by bit 3 of r, conflict-free; an XOR by (r / 2) % 8 left 43% of the
+// LDS's active cycles stalled on bank conflicts (1% slower).  Rows of 64 bytes
+// (bf16): by (r / 4) % 4; on this part every placement of 64-byte rows tried
+// (other XORs, none) costs a second pass per read, half the LDS cycles, which
+// the MFMAs hide (a conflict-free piece-major layout was 5% slower, its
+// direct loads touching four times as many rows per instruction).  An
+// involution for each row, so it also maps slots back to pieces.
 template <int CB>
 __device__ __forceinline__ int piece_slot(int r, int c) {
     static_assert(CB == 64 || CB == 128 || CB % 256 == 0, "chunk of 64, 128 or a multiple of 256 bytes per row");
-    return CB >= 256 ? (c ^ (r & 15)) : CB == 128 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
+    return CB >= 256   ? (c ^ (r & 15))
+           : CB == 128 ? (c ^ ((r & 7) ^ ((r >> 3) & 1)))
+                       : (c ^ ((r >> 2) & 3));
 }
 
 // Per type: the MFMA step KS (reduction elements), element size, the packed
