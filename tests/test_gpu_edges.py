@@ -161,6 +161,31 @@ def test_tiled_bf16_chunk_counts(H, I):
     _compare(cfg, np_of(r["out"]), ref, "tiled bf16 H=%d I=%d" % (H, I))
 
 
+@pytest.mark.parametrize("dtype", ["fp8", "fp8u"])
+@pytest.mark.parametrize("H,I", [(256, 256), (768, 512), (1280, 768)])
+def test_tiled_fp8_chunk_counts(dtype, H, I):
+    """fp8 (fp32 and power-of-two scales) through the 128-row kernels
+    (256-byte chunks, two ring slots, direct loads issued from assembly) for
+    reduction lengths of one chunk and of odd and even chunk counts (gate/up /
+    down: 1 / 1, 3 / 2, 5 / 3 chunks), with ragged experts; every output row
+    against the oracle."""
+    m = rdg()
+    cfg = dict(_cfg(dtype, H=H, I=I, N=4, K=2, wid=790 + H + I), n_group=2, topk_group=1)
+    T = 300
+    logits = synth.logits(cfg, T)
+    ri, rw = oracle.route(logits, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+    x, x_s, xo, xo_s = _inputs(cfg, T)
+    experts = ExpertSet(cfg, range(cfg["N"]))
+    r = run_routed(cfg, x, x_s, torch.from_numpy(ri).to(DEV), torch.from_numpy(rw).to(DEV), experts,
+                   m.RDG_CONTIGUOUS, block_m=128)
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    DT = m.RDG_FP8_E4M3_UE8M0 if dtype == "fp8u" else m.RDG_FP8_E4M3
+    assert m.rdg_signal_rows(r["L"], DT, H, I) == 128  # the row tile the FFN ran with
+    ref = oracle.moe_layer(dt_code(cfg), xo, ri, rw, [experts.oracle_expert(j) for j in range(cfg["N"])],
+                           x_scales=xo_s)
+    _compare(cfg, np_of(r["out"]), ref, "tiled %s H=%d I=%d" % (dtype, H, I))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8"])
 @pytest.mark.parametrize("kind", [0, 1])
 def test_weight_streaming_experts_over_several_tiles(dtype, kind):
