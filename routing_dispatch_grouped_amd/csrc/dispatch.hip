@@ -149,10 +149,26 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
                                                int32_t* __restrict__ masked_m, int32_t* __restrict__ tile_off,
                                                int32_t* __restrict__ status, int64_t* __restrict__ expert_load) {
     __shared__ int lds[32];
+    __shared__ int cells[1024];
     const int e = threadIdx.x;
     const bool act = e < n_local;
     int run = 0;
-    if (act) {
+    const int64_t n_cells = (int64_t)n_local * n_chunks;
+    if (n_cells <= 1024) {
+        // every (chunk, expert) count in one round of loads, one per thread;
+        // each expert's thread scans its column from LDS
+        if (e < n_cells) cells[e] = chunk_counts[e];
+        __syncthreads();
+        if (act) {
+            for (int c = 0; c < n_chunks; ++c) {
+                const int v = cells[c * n_local + e];
+                cells[c * n_local + e] = run;
+                run += v;
+            }
+        }
+        __syncthreads();
+        if (e < n_cells) chunk_counts[e] = cells[e];
+    } else if (act) {
         int c = 0;
         for (; c + 8 <= n_chunks; c += 8) {  // issue eight independent loads, then scan them
             int v[8];
@@ -170,6 +186,8 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
             *p = run;
             run += v;
         }
+    }
+    if (act) {
         counts[e] = run;
         // the expert-load recorder: routed rows before any capacity drop
         if (expert_load != nullptr)
