@@ -23,9 +23,13 @@ Five workloads, named by what they are:
                      follows the group-limited rule, the "simulated perfect
                      EPLB" expert distribution (balanced in expectation).
 * ``decode_rank_fp8`` one decode rank's share with EPLB: 72 ranks x 4
-                     physical experts (256 logical + 32 replicas), the
-                     bottleneck rank receives 1024 token-expert rows; fp8
-                     e4m3 with 1x128 / 128x128 block scales; masked layout.
+                     physical experts (256 logical + 32 redundant copies,
+                     each given greedily to the expert with the largest
+                     expected load per copy; ``replicas="one_each"`` gives
+                     the 32 most popular experts one extra copy each
+                     instead), the bottleneck rank receives 1024
+                     token-expert rows; fp8 e4m3 with 1x128 / 128x128 block
+                     scales; masked layout.
 * ``prefill_rank_fp8`` one prefill rank's share: 32 ranks x 9 physical
                      experts, 16384 received rows, shared expert on the
                      rank's own 2048 tokens; fp8; contiguous layout; the
@@ -162,30 +166,54 @@ def expert_weights(cfg, e, device="cpu", shared=False):
                 W2=normal(cfg["wid"], base + 2, e, (H, I), WEIGHT_STD, device, dt))
 
 
-def eplb_plan(cfg):
-    """Static placement of 256 logical experts into n_ranks * n_local slots.
+def replica_counts(pop, n_redundant, rule="greedy"):
+    """Copies of each logical expert (workload recipe, not a hot-path step).
 
-    Workload recipe (the placement algorithm itself is not on the hot path):
-    the n_redundant most popular logical experts (expected Zipf popularity)
-    get a second replica; physical experts, each carrying popularity /
-    replicas, are taken in descending load (ties: lower logical id, then
-    replica index) and each goes to the least-loaded rank that still has a
-    free slot (ties: lower rank).  Physical id = rank * n_local + slot.
-    Returns log2phy [N, 2], n_replica [N], rank loads, and the bottleneck
-    rank (highest expected load, ties lower rank).
+    greedy:   n_redundant times, one more copy to the logical expert with the
+              largest expected load per copy (ties: lower id) -- the replica
+              rule of the EPLB workloads.
+    one_each: the n_redundant most popular experts get one extra copy each
+              (ties: lower id), a plainer allocation kept for comparison.
+    """
+    N = len(pop)
+    n_rep = np.ones(N, np.int32)
+    if rule == "one_each":
+        for e in sorted(range(N), key=lambda e: (-pop[e], e))[:n_redundant]:
+            n_rep[e] = 2
+        return n_rep
+    if rule != "greedy":
+        raise ValueError(rule)
+    for _ in range(n_redundant):
+        per_copy = pop / n_rep
+        best = max(per_copy)
+        e = int(np.flatnonzero(per_copy == best)[0])
+        n_rep[e] += 1
+    return n_rep
+
+
+def eplb_plan(cfg, rule=None):
+    """Static placement of the logical experts into n_ranks * n_local slots.
+
+    Workload recipe (the placement itself is not on the hot path): copies per
+    expert from replica_counts (cfg["replicas"], default greedy); physical
+    experts, each carrying expected popularity / copies, are taken in
+    descending load (ties: lower logical id, then copy index) and each goes
+    to the least-loaded rank that still has a free slot (ties: lower rank).
+    Physical id = rank * n_local + slot.  Returns log2phy [N, r_max] (unused
+    columns repeat the first copy), n_replica [N], the expected rank loads,
+    and the bottleneck rank (highest expected load, ties lower rank).
     """
     N, n_ranks, n_local = cfg["N"], cfg["n_ranks"], cfg["n_local"]
     assert n_ranks * n_local == N + cfg["n_redundant"]
+    rule = rule or cfg.get("replicas", "greedy")
     pop = expected_popularity(cfg)
-    order = sorted(range(N), key=lambda e: (-pop[e], e))
-    n_rep = np.ones(N, np.int32)
-    for e in order[:cfg["n_redundant"]]:
-        n_rep[e] = 2
+    n_rep = replica_counts(pop, cfg["n_redundant"], rule)
+    r_max = int(n_rep.max())
     units = [(pop[e] / n_rep[e], e, r) for e in range(N) for r in range(n_rep[e])]
     units.sort(key=lambda u: (-u[0], u[1], u[2]))
     load = np.zeros(n_ranks)
     used = np.zeros(n_ranks, np.int64)
-    log2phy = np.full((N, 2), -1, np.int32)
+    log2phy = np.full((N, r_max), -1, np.int32)
     for ld, e, r in units:
         cand = [k for k in range(n_ranks) if used[k] < n_local]
         k = min(cand, key=lambda k: (load[k], k))
@@ -193,11 +221,10 @@ def eplb_plan(cfg):
         used[k] += 1
         load[k] += ld
     for e in range(N):
-        if n_rep[e] == 1:
-            log2phy[e, 1] = log2phy[e, 0]
+        log2phy[e, n_rep[e]:] = log2phy[e, 0]
     bottleneck = int(np.argmax(load))
     return dict(log2phy=log2phy, n_replica=n_rep, load=load, bottleneck=bottleneck,
-                phys_begin=bottleneck * n_local, n_local=n_local)
+                phys_begin=bottleneck * n_local, n_local=n_local, rule=rule)
 
 
 def take_rank_rows(local_ids, rows):
