@@ -41,6 +41,8 @@ def lib():
         P = ctypes.c_void_p
         i32, i64, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_float
         L.orc_num_threads.restype = i32
+        L.orc_set_num_threads.argtypes = [i32]
+        L.orc_set_num_threads.restype = i32
         L.orc_bf16_decode.argtypes = [ctypes.c_uint16]
         L.orc_bf16_decode.restype = ctypes.c_double
         L.orc_bf16_encode.argtypes = [ctypes.c_double]
@@ -55,6 +57,8 @@ def lib():
         L.orc_sigmoid.argtypes = [f32]
         L.orc_sigmoid.restype = f32
         L.orc_sigmoid_many.argtypes = [P, P, i64]
+        L.orc_sigmoid_constants.argtypes = [P]
+        L.orc_sigmoid_constants.restype = None
         L.orc_sigmoid_sweep.argtypes = [ctypes.c_uint32, ctypes.c_uint32, ctypes.c_uint32,
                                         ctypes.POINTER(i64), ctypes.POINTER(i64)]
         L.orc_sigmoid_sweep.restype = ctypes.c_double
@@ -81,6 +85,11 @@ def _p(a):
 
 def num_threads():
     return lib().orc_num_threads()
+
+
+def set_num_threads(n):
+    """Threads of the oracle's parallel loops from now on; returns the previous count."""
+    return lib().orc_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- formats
@@ -129,6 +138,14 @@ def sigmoid(x):
     y = np.empty_like(x)
     lib().orc_sigmoid_many(_p(x), _p(y), x.size)
     return y
+
+
+def sigmoid_constants():
+    """The oracle's sigmoid constants as derived at run time: log2(e), the
+    two-part ln 2 (head, tail), then 1/k! for k = 0..13 (doubles)."""
+    out = np.empty(17, dtype=np.float64)
+    lib().orc_sigmoid_constants(_p(out))
+    return out
 
 
 def sigmoid_sweep(lo_bits, hi_bits, stride):

@@ -54,6 +54,18 @@ int orc_num_threads(void) {
 #endif
 }
 
+/* Threads for the parallel loops that follow (n >= 1); for timing the
+ * oracle single-threaded.  Returns the previous count. */
+int orc_set_num_threads(int n) {
+    int old = orc_num_threads();
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+    return old;
+}
+
 /* ------------------------------------------------------------------------
  * Number formats.
  * ------------------------------------------------------------------------ */

@@ -219,3 +219,24 @@ def check_rows(got, ref, cfg, what=""):
 def tolerance(cfg):
     """Max relative error max|out-ref|/max|ref| allowed per tensor."""
     return {"f32": 1e-5, "bf16": 2e-2, "fp8": 6e-2, "fp8u": 6e-2}[cfg["dtype"]]
+
+
+def ue8m0_clamp_edge_rows(seed=11):
+    """fp32 rows of 128 whose largest magnitude sits at the lower clamp of
+    power-of-two block scales (2^-126): exactly 448 * 2^-126, one ulp either
+    side of it, 448 * 2^-127 and 2^-126 (clamped), fp32-subnormal blocks,
+    and an all-zero block.  Elements are random multiples of the block's
+    amax, so the smallest of them are fp32 subnormals."""
+    rng = np.random.default_rng(seed)
+    edge = np.float32(448.0 * 2.0 ** -126)
+    amaxes = [edge, np.nextafter(edge, np.float32(np.inf)), np.nextafter(edge, np.float32(0)),
+              np.float32(448.0 * 2.0 ** -127), np.float32(2.0 ** -126), np.float32(2.0 ** -133),
+              np.float32(2.0 ** -140), np.float32(2.0 ** -149), np.float32(1.5 * 448.0 * 2.0 ** -126),
+              np.float32(0.0)]
+    rows = []
+    for a in amaxes:
+        for rep in range(3):
+            v = (rng.uniform(-1.0, 1.0, 128) * np.float64(a)).astype(np.float32)
+            v[rng.integers(128)] = a if rep != 1 else -a
+            rows.append(v)
+    return np.array(rows, dtype=np.float32)

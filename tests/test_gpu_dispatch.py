@@ -139,6 +139,32 @@ def test_quantiser_bit_exact(rows, cols, block_rows, src):
     assert np.array_equal(np_of(q), rq)
 
 
+@pytest.mark.parametrize("block_rows", [1, 128])
+def test_quantiser_ue8m0_clamp_edge(block_rows):
+    # power-of-two scales at their lower clamp (2^-126), fp32-subnormal
+    # blocks and an all-zero block: device codes and scales equal the oracle's
+    from harness import ue8m0_clamp_edge_rows
+    m = rdg()
+    rows = ue8m0_clamp_edge_rows()
+    if block_rows == 128:
+        # 128 x 128 weight blocks: each block's rows scaled to one edge row's amax
+        v = np.concatenate([np.tile(rows[i:i + 1], (128, 1)) * np.float32(0.5) for i in range(0, len(rows), 3)])
+        for b in range(len(v) // 128):
+            v[b * 128 + 17] = rows[3 * b]     # the edge amax itself, inside the block
+        v = np.concatenate([v, v[:, ::-1]], 1)   # two column blocks
+    else:
+        v = rows
+    R, C = v.shape
+    t = torch.from_numpy(np.ascontiguousarray(v)).to(DEV)
+    q = torch.empty((R, C), dtype=torch.uint8, device=DEV)
+    s = torch.empty(((R + block_rows - 1) // block_rows, C // 128), dtype=torch.float32, device=DEV)
+    m.rdg_quantize_fp8_ue8m0(t, m.RDG_F32, block_rows, q, s)
+    rq, rs = oracle.quantize_fp8(np.ascontiguousarray(v), block_rows, ue8m0=True)
+    assert (rs[rs != 1.0] <= 2.0 ** -125).all()
+    assert np.array_equal(np_of(s), rs)
+    assert np.array_equal(np_of(q), rq)
+
+
 def test_expert_load_recorder():
     """rdg_dispatch accumulates each expert's routed rows (before capacity
     drops) into the layout's expert_load buffer across calls."""

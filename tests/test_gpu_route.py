@@ -95,3 +95,54 @@ def test_route_biased(B, N, n_group, topk_group, K, std):
         assert len(bad) == 0, (bad[:10], gi[bad[:3]], ri[bad[:3]])
         bound = (K + 2) * 2.0 ** -24
         assert np.max(np.abs(gw.astype(np.float64) - rw) / np.maximum(np.abs(rw), 1e-30)) <= bound
+
+
+def _sigmoid_boundary_cases(n_cases, seed=901):
+    """Logits whose fp64 sigmoid lies closest to an fp32 rounding boundary
+    (a 1-ulp difference between two evaluations is most likely there), each
+    with a partner logit whose oracle sigmoid is the same fp32 value.  Two
+    tokens per case over two experts in one group, K = 1: [partner, x] and
+    [x, partner].  Both are ties under the oracle, so the lower index wins;
+    a device sigmoid one ulp above the oracle's at x picks expert 1 in the
+    first token, one ulp below picks expert 1 in the second."""
+    rng = np.random.default_rng(seed)
+    x = rng.uniform(-12.0, 12.0, 1 << 21).astype(np.float32)
+    s = oracle.sigmoid(x)
+    up = np.nextafter(s, np.float32(2.0))
+    dn = np.nextafter(s, np.float32(-1.0))
+    s64 = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    mid_up = (s.astype(np.float64) + up) / 2
+    mid_dn = (s.astype(np.float64) + dn) / 2
+    ulp = (up.astype(np.float64) - s)
+    dist = np.minimum(np.abs(s64 - mid_up), np.abs(s64 - mid_dn)) / ulp
+    # the hardest cases of each of 16 logit ranges, so that the whole curve is covered
+    bins = np.floor((x.astype(np.float64) + 12.0) / 1.5).astype(np.int64)
+    order = np.lexsort((dist, bins))
+    rank = np.empty_like(order)
+    starts = np.searchsorted(bins[order], np.arange(16))
+    rank[order] = np.arange(len(order)) - starts[bins[order]]
+    pairs = []
+    for i in np.argsort(rank, kind="stable"):
+        xi = x[i]
+        for step in (1, -1, 2, -2, 3, -3, 4, -4):
+            y = xi
+            for _ in range(abs(step)):
+                y = np.nextafter(y, np.float32(np.inf if step > 0 else -np.inf))
+            if oracle.sigmoid(np.array([y]))[0] == s[i]:
+                pairs.append((y, xi, dist[i]))
+                break
+        if len(pairs) == n_cases:
+            break
+    return pairs
+
+
+def test_route_sigmoid_rounding_boundaries():
+    pairs = _sigmoid_boundary_cases(4096)
+    assert len(pairs) == 4096
+    print("sigmoid boundary cases: largest distance from a rounding boundary %.3e ulp" % pairs[-1][2], flush=True)
+    lg = np.array([[y, x] for y, x, _ in pairs] + [[x, y] for y, x, _ in pairs], dtype=np.float32)
+    gi, _ = _run(lg, 1, 1, 1)
+    ri, _ = oracle.route(lg, 1, 1, 1)
+    assert (ri == 0).all()  # every token is a tie under the oracle
+    bad = np.flatnonzero(gi[:, 0] != ri[:, 0])
+    assert len(bad) == 0, ("device sigmoid differs from the oracle's at logits", lg[bad[:8]])

@@ -130,3 +130,28 @@ def test_ue8m0_matches_fp32_rule_at_exact_powers(orc):
         assert sb[r, 0] == 2.0 ** j and sa[r, 0] == sb[r, 0]
         assert np.array_equal(qa[r, :128], qb[r, :128])
         assert sb[r, 1] == 2.0 ** (j + 1)
+
+
+def test_ue8m0_clamp_edge(orc):
+    # amax at and below 448 * 2^-126: the power-of-two scale stops at 2^-126
+    # (the smallest normal fp32 and the lowest 8-bit exponent kept), so the
+    # codes are the nearest e4m3 values of v * 2^126; checked against the
+    # closed form of the scale with its clamp and a brute-force nearest-even
+    # encoder over the 127 non-negative finite codes
+    from harness import ue8m0_clamp_edge_rows
+    x = ue8m0_clamp_edge_rows()
+    q, s = orc.quantize_fp8(x, 1, ue8m0=True)
+    amax = np.abs(x).max(1).astype(np.float64)
+    want_s = np.where(amax > 0, np.maximum(2.0 ** np.ceil(np.log2(np.maximum(amax, 1e-300) / 448.0)), 2.0 ** -126), 1.0)
+    assert np.array_equal(s[:, 0].astype(np.float64), want_s)
+    assert (s[:-3, 0] <= 2.0 ** -125).all()
+    table = orc.fp8_decode(np.arange(127))
+    t = np.abs(x.astype(np.float64)) / want_s[:, None]          # exact: a power-of-two scale
+    d = np.abs(t[..., None] - table)
+    best = d.min(-1, keepdims=True)
+    cand = d == best
+    # ties to the even code (the one with a zero last mantissa bit)
+    code = np.where(cand.sum(-1) > 1, np.argmax(cand & (np.arange(127) % 2 == 0), -1), np.argmax(cand, -1))
+    code = code | np.where(np.signbit(x) & (code > 0), 0x80, 0)
+    mag_q = q & 0x7f
+    assert np.array_equal(np.where(mag_q == 0, 0, q), code.astype(np.uint8))
