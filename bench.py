@@ -1,23 +1,30 @@
 """Benchmark of the MoE-layer hot path on one MI355X.
 
 A step is one pass of the whole hot path over one batch of seeded synthetic
-input already resident in HBM.  The default workload (the one the JSON line
-reports) is the DeepSeek-V3-shaped decode layer with every expert on this
-GPU: 128 tokens, H=7168, 256 experts in 8 groups of 32, 4 groups kept,
-top-8, I=2048, shared expert I=2048, bf16, masked layout with 256 rows per expert.  Its step:
-route -> dispatch -> grouped gate/up GEMM (+SiLU-gated product) -> grouped
-down GEMM -> combine, with the shared expert on a second stream overlapping
-everything before the combine.
+input already resident in HBM.  The default workload -- the one the JSON
+line's value reports -- is the largest layer that runs on one GPU: the
+DeepSeek-V3-shaped prefill layer with every expert on this GPU, 4096 tokens
+(two 2048-token sequences), H=7168, 256 experts in 8 groups of 32, 4 groups
+kept, top-8, I=2048, shared expert I=2048, bf16, expert popularity Zipf(1.1),
+contiguous layout padded to 128 rows.  Its step: route -> dispatch ->
+grouped gate/up GEMM (+SiLU-gated product) -> grouped down GEMM -> combine,
+with the shared expert on a second stream overlapping everything before the
+combine.
 
---workload selects the other layers the parity tests cover (tiny fp32,
-4096-token bf16 prefill, and the fp8 decode / prefill rank shares with EPLB
+--workload selects another layer (tiny fp32, the 128-token decode layer, the
+balanced prefill layer, and the fp8 decode / prefill rank shares with EPLB
 remap; the prefill share overlaps its signalled down GEMM and the shared
 expert with a polling combine on a second stream).
 
 Extra fields: "roofline" for the dominant kernel (the grouped gate/up GEMM,
-timed with HIP events on the stream it is launched on) and "cpu_baseline"
-(the CPU oracle timed on a bounded sample of the same workload on this host,
-default workload only).
+timed with HIP events on the stream it is launched on), "layer" (the whole
+step against HBM), "cpu_baseline" (the CPU oracle timed on a bounded sample
+of the same workload on this host), for the prefill layer "heavy_experts"
+(the gate/up and down GEMMs over the experts with at least 315 rows, where
+the bf16 MFMA rate can show), for the prefill rank share "sbo" (the step
+with the signalled down GEMM and polling combine against the same step run
+sequentially), and with the default workload "workloads": the same figures
+for every other configuration, each measured in this run.
 """
 import argparse
 import json
@@ -31,6 +38,16 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "prefill_bf16"
+ALL_WORKLOADS = ["tiny_fp32", "decode_bf16", "prefill_bf16", "prefill_bf16_balanced", "decode_rank_fp8",
+                 "prefill_rank_fp8"]
+# tokens of the CPU oracle's FFN sample per workload (routing / remap and the
+# layout always cover the whole batch); chosen for a few to about 20 seconds
+# of oracle time on 16 host threads
+CPU_TOKENS = {"tiny_fp32": -1, "decode_bf16": -1, "prefill_bf16": 192, "prefill_bf16_balanced": 96,
+              "decode_rank_fp8": 256, "prefill_rank_fp8": 256}
+SUMMARY_CPU_TOKENS = {"tiny_fp32": -1, "decode_bf16": 32, "prefill_bf16_balanced": 0, "decode_rank_fp8": 64,
+                      "prefill_rank_fp8": 64, "prefill_bf16": 48}
 
 
 def parse():
@@ -38,19 +55,23 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--workload", default="decode_bf16",
-                   choices=["decode_bf16", "tiny_fp32", "prefill_bf16", "prefill_bf16_balanced", "decode_rank_fp8",
-                            "prefill_rank_fp8"])
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=ALL_WORKLOADS)
+    p.add_argument("--summary", choices=["auto", "on", "off"], default="auto",
+                   help="also measure every other workload and report it under 'workloads' (auto: with the "
+                        "default workload and no variant flags)")
     p.add_argument("--graph", action="store_true",
                    help="time replays of the step captured in a HIP graph (full-layer workloads); the gate/up "
                         "kernel's own time then comes from as many eager steps run after them")
     p.add_argument("--ue8m0", action="store_true",
                    help="fp8 workloads with power-of-two block scales (scaled-MFMA path)")
+    p.add_argument("--eplb-replicas", choices=["greedy", "one_each"], default=None,
+                   help="rank shares: the EPLB plan's replica rule (default greedy: each of the 32 redundant "
+                        "copies to the expert with the largest expected load per copy)")
     p.add_argument("--tbo", action="store_true",
                    help="prefill layers as two micro-batches cut at a sequence boundary, on two streams "
                         "(the roofline then covers micro-batch A's gate/up)")
-    p.add_argument("--cpu-tokens", type=int, default=-1,
-                   help="tokens in the CPU-oracle sample (-1: the whole batch; 0: skip)")
+    p.add_argument("--cpu-tokens", type=int, default=None,
+                   help="tokens in the CPU-oracle FFN sample (-1: the whole batch; 0: skip; default per workload)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="after the timed region, copy 1 GiB device-to-device twice (a plain copy kernel of known "
                         "size, for scaling the FETCH_SIZE / WRITE_SIZE counters of a profiling run)")
@@ -60,8 +81,9 @@ def parse():
 # Files whose contents determine the dominant kernel's memory traffic (the
 # kernel, its device helpers and the packed weight layout); the committed
 # counter figures apply only while their hash is unchanged.
-TRAFFIC_SOURCES = ["routing_dispatch_grouped_amd/csrc/ffn.hip", "routing_dispatch_grouped_amd/csrc/rdg_internal.h",
-                   "routing_dispatch_grouped_amd/csrc/pack.hip"]
+TRAFFIC_SOURCES = ["routing_dispatch_grouped_amd/csrc/ffn.hip", "routing_dispatch_grouped_amd/csrc/ffn_tiled.hip",
+                   "routing_dispatch_grouped_amd/csrc/rdg_internal.h", "routing_dispatch_grouped_amd/csrc/pack.hip",
+                   "routing_dispatch_grouped_amd/csrc/abi.hip"]
 
 
 def source_hash():
@@ -119,14 +141,20 @@ def layer_bytes(cfg, T, R, A, esz):
 class Bench:
     """Buffers and the step of one workload."""
 
-    def __init__(self, name, dev, ue8m0=False, tbo=False):
+    def __init__(self, name, dev, ue8m0=False, tbo=False, replicas=None):
         import torch
 
         import routing_dispatch_grouped_amd as rdg
         import synth
         self.torch, self.rdg, self.synth = torch, rdg, synth
         self.name, self.dev = name, dev
-        self.cfg = cfg = synth.WORKLOADS[name]
+        self.cfg = cfg = dict(synth.WORKLOADS[name])
+        if replicas and "B_global" in cfg:
+            cfg["replicas"] = replicas
+        # prefill rank share: "signalled" (down GEMM publishes row tiles, a
+        # polling combine overlaps it) or "sequential" (plain down GEMM, then
+        # a plain combine on the same stream)
+        self.sbo_mode = "signalled"
         self.DT = {"f32": rdg.RDG_F32, "bf16": rdg.RDG_BF16, "fp8": rdg.RDG_FP8_E4M3}[cfg["dtype"]]
         # fp8 with power-of-two block scales: same codes and layouts, scales
         # applied inside the scaled MFMA by the 128-row kernels
@@ -337,7 +365,8 @@ class Bench:
         for e in range(cfg["N"]):
             for r in range(plan["n_replica"][e]):
                 phys2log[plan["log2phy"][e, r]] = e
-        self.W, self.S = self._experts([int(phys2log[plan["phys_begin"] + s]) for s in range(plan["n_local"])])
+        self.local_logical = [int(phys2log[plan["phys_begin"] + s]) for s in range(plan["n_local"])]
+        self.W, self.S = self._experts(self.local_logical)
         kind = rdg.RDG_MASKED if cfg["layout"] == "masked" else rdg.RDG_CONTIGUOUS
         self._buffers(T, K, plan["n_local"], kind, block_m=128, m_max=cfg.get("m_max", 0))
         self.out = torch.empty((T, cfg["H"]), dtype=self.ydt, device=self.dev)
@@ -409,6 +438,17 @@ class Bench:
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
             return
+        if self.sbo_mode == "sequential":
+            # the same step without the overlap: shared expert on the side
+            # stream beside gate/up, then down GEMM and a plain combine
+            self.side.wait_stream(self.stream)
+            self._gate_up(timed)
+            with self.torch.cuda.stream(self.side):
+                self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
+            rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
+            rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
+            self.stream.wait_stream(self.side)
+            return
         # signalled down GEMM on this stream; on the side stream the shared
         # expert (overlapping gate/up), then the polling combine, released once
         # gate/up is done so that it overlaps the down GEMM
@@ -426,34 +466,69 @@ class Bench:
         self.stream.wait_stream(self.side)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1:
-        print("bench.py measures one GPU's share of the layer; runs on several GPUs (--gpus %d) are not "
-              "supported (the expert-parallel sharding is described, not implemented)" % args.gpus, file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
-    import torch
-
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo)
-    rdg, cfg = b.rdg, b.cfg
-    for _ in range(args.warmup):
-        b.step()
+def _ms_steps(b, steps, timed=True):
+    """Wall-clock ms per step over `steps` steps (synchronised on both
+    sides) and the mean gate/up kernel time recorded on its stream."""
+    torch = b.torch
+    b.events = []
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        b.step(timed=timed)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    gate = None
+    if b.events:
+        import numpy as np
+        gate = float(np.mean([a.elapsed_time(e) for a, e in b.events]))
+    return (t1 - t0) * 1e3 / steps, gate
+
+
+def _stats(b):
+    rdg = b.rdg
     code, detail = rdg.rdg_check_status(b.L)
     if code != 0:
         raise RuntimeError("device status %d (%s), detail %d" % (code, rdg.strerror(code), detail))
     masked_m = b.L.masked_m.cpu().numpy()
-    active = int((masked_m > 0).sum())
-    rows = int(masked_m.sum())
     counts = b.L.counts.cpu().numpy()
     # load balance of the local experts, mean / max of their routed rows (the
     # statistic expert-load rebalancing raises)
     balance = float(counts.mean() / counts.max()) if counts.max() > 0 else 1.0
+    return int((masked_m > 0).sum()), int(masked_m.sum()), balance, masked_m
 
+
+def _roofline(cfg, active, rows, gate_ms, workload):
+    """Roofline of one gate/up launch: algorithmic bytes (W1 and W3 of every
+    active expert, + fp8 block scales; the routed rows of x_perm read once, h
+    written once) and flops 4 R H I; the bound is whichever of bytes / 8 TB/s
+    and flops / MFMA peak is the longer."""
+    H, I = cfg["H"], cfg["I"]
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg["dtype"]]
+    gate_bytes = active * 2 * I * H * esz + rows * H * esz + rows * I * esz
+    if esz == 1:
+        gate_bytes += active * 2 * (I // 128) * (H // 128) * 4 + rows * (H // 128 + I // 128) * 4
+    gate_flops = 2 * 2 * rows * H * I
+    gbps = gate_bytes / (gate_ms * 1e-3) / 1e9
+    tflops = gate_flops / (gate_ms * 1e-3) / 1e12
+    peak_f = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+    hbm_frac, mfma_frac = gbps / HBM_PEAK_GBPS, tflops / peak_f
+    hbm_bound = gate_bytes / (HBM_PEAK_GBPS * 1e9) >= gate_flops / (peak_f * 1e12)
+    return {"kernel": "grouped gate/up GEMM + SiLU-gated product (%s)" % cfg["dtype"],
+            "bound": "hbm" if hbm_bound else "mfma",
+            "achieved": gbps if hbm_bound else tflops, "peak": HBM_PEAK_GBPS if hbm_bound else peak_f,
+            "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": hbm_frac if hbm_bound else mfma_frac,
+            "traffic": measured_traffic(workload), "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes,
+            "algorithmic_flops": gate_flops, "source_hash": source_hash(),
+            "hbm_frac": hbm_frac, "mfma_frac": mfma_frac}
+
+
+def measure(b, args, steps, warmup, workload):
+    """Warm-up, the timed steps, and the JSON fields of one workload."""
+    torch, cfg = b.torch, b.cfg
+    for _ in range(warmup):
+        b.step()
     torch.cuda.synchronize()
+    active, rows, balance, _ = _stats(b)
     if args.graph:
         if b.rank:
             raise SystemExit("--graph covers the full-layer workloads")
@@ -463,50 +538,23 @@ def main():
         graph.replay()
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(args.steps):
+        for _ in range(steps):
             graph.replay()
         torch.cuda.synchronize()
-        t1 = time.perf_counter()
-        for _ in range(args.steps):
-            b.step(timed=True)
-        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        _, gate_ms = _ms_steps(b, steps)
     else:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            b.step(timed=True)
-        torch.cuda.synchronize()
-        t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    gate_ms = float(np.mean([a.elapsed_time(e) for a, e in b.events]))
-
+        ms, gate_ms = _ms_steps(b, steps)
     H, I, K = cfg["H"], cfg["I"], cfg["K"]
     esz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg["dtype"]]
-    # algorithmic work of one gate/up launch: W1 and W3 of every active expert
-    # (+ fp8 block scales), the routed rows of x_perm read once, h written once
-    gate_bytes = active * 2 * I * H * esz + rows * H * esz + rows * I * esz
-    if esz == 1:
-        gate_bytes += active * 2 * (I // 128) * (H // 128) * 4 + rows * (H // 128 + I // 128) * 4
-    gate_flops = 2 * 2 * rows * H * I
-    gbps = gate_bytes / (gate_ms * 1e-3) / 1e9
-    tflops = gate_flops / (gate_ms * 1e-3) / 1e12
-    peak_f = MFMA_PEAK_TFLOPS[cfg["dtype"]]
-    hbm_frac, mfma_frac = gbps / HBM_PEAK_GBPS, tflops / peak_f
-    # the bound is the resource the roofline says limits this launch
-    hbm_bound = gate_bytes / (HBM_PEAK_GBPS * 1e9) >= gate_flops / (peak_f * 1e12)
-    roof = {"kernel": "grouped gate/up GEMM + SiLU-gated product (%s)" % cfg["dtype"],
-            "bound": "hbm" if hbm_bound else "mfma",
-            "achieved": gbps if hbm_bound else tflops, "peak": HBM_PEAK_GBPS if hbm_bound else peak_f,
-            "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": hbm_frac if hbm_bound else mfma_frac,
-            "traffic": measured_traffic(args.workload), "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes,
-            "algorithmic_flops": gate_flops, "source_hash": source_hash(),
-            "hbm_frac": hbm_frac, "mfma_frac": mfma_frac}
+    roof = _roofline(cfg, active, rows, gate_ms, workload)
     if b.rank:
         metric, unit = "MoE-layer token-equivalents/s (received rows / K) on 1 MI355X", "token-equivalents/s"
         value = rows / K / (ms * 1e-3)
     else:
         metric, unit = "MoE-layer tokens/s on 1 MI355X", "tokens/s"
         value = b.T / (ms * 1e-3)
-    conf = {"workload": args.workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
+    conf = {"workload": workload, "tokens": b.T, "H": H, "I": I, "K": K, "experts": cfg["N"],
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
             "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph),
@@ -518,17 +566,103 @@ def main():
     if "m_max" in cfg:
         conf["m_max"] = cfg["m_max"]
     if b.rank:
-        conf.update(local_experts=cfg["n_local"], ranks=cfg["n_ranks"], received_rows=rows)
-    # the whole step against HBM: every kernel's algorithmic bytes over the step time
+        conf.update(local_experts=cfg["n_local"], ranks=cfg["n_ranks"], received_rows=rows,
+                    eplb_replicas=b.plan["rule"], rows_per_local_expert=b.L.masked_m.cpu().tolist())
     lb = layer_bytes(cfg, b.T, rows, active, esz)
     layer = {"algorithmic_bytes": lb, "achieved": lb / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
-    line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": cfg["dtype"], "data": "synthetic", "config": conf, "roofline": roof, "layer": layer}
-    if args.cpu_tokens != 0 and not b.rank and args.workload == "decode_bf16":
-        n_tok = b.logits_np.shape[0] if args.cpu_tokens < 0 else min(args.cpu_tokens, b.logits_np.shape[0])
-        line["cpu_baseline"] = cpu_baseline(b, n_tok)
+    return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms, "dtype": cfg["dtype"],
+            "config": conf, "roofline": roof, "layer": layer}
+
+
+def sbo_compare(b, steps, rounds=4):
+    """The prefill rank share's step with the signalled down GEMM and the
+    polling combine against the same step run sequentially (plain down GEMM,
+    then a plain combine), timed in alternating blocks."""
+    import numpy as np
+    per = max(3, steps // 2)
+    res = {"signalled": [], "sequential": []}
+    for _ in range(rounds):
+        for mode in ("signalled", "sequential"):
+            b.sbo_mode = mode
+            b.step()
+            ms, _ = _ms_steps(b, per, timed=False)
+            res[mode].append(ms)
+    b.sbo_mode = "signalled"
+    sig, seq = float(np.median(res["signalled"])), float(np.median(res["sequential"]))
+    return {"signalled_ms": sig, "sequential_ms": seq, "gain_ms": seq - sig,
+            "overlap_pays": seq > sig, "rounds": rounds, "steps_per_round": per}
+
+
+def heavy_experts(b, min_rows=315, reps=5):
+    """The routed GEMMs restricted to the experts with at least `min_rows`
+    rows (the rows per expert from which a bf16 tile's arithmetic outweighs
+    its expert's weight bytes: 2.5 PFLOP/s / 8 TB/s), timed on their own:
+    all of them in one grouped launch (the same kernels, the other experts'
+    rows masked out of the dispatch), and each expert alone."""
+    import numpy as np
+    torch, rdg, cfg = b.torch, b.rdg, b.cfg
+    H, I, K, N = cfg["H"], cfg["I"], cfg["K"], cfg["N"]
+    counts = b.L.counts.cpu().numpy()
+    heavy = [int(e) for e in np.flatnonzero(counts >= min_rows)]
+    if not heavy:
+        return None
+    peak = MFMA_PEAK_TFLOPS[cfg["dtype"]]
+
+    def run(expert_set):
+        keep = torch.zeros(N, dtype=torch.bool, device=b.dev)
+        keep[expert_set] = True
+        ids = torch.where(keep[b.ids.long()], b.ids, torch.full_like(b.ids, -1))
+        L = rdg.Layout(rdg.RDG_CONTIGUOUS, N, b.T, K, b.dev, block_m=128)
+        xp = torch.empty((L.m_cap, H), dtype=b.sdt, device=b.dev)
+        h = torch.empty((L.m_cap, I), dtype=b.sdt, device=b.dev)
+        y = torch.empty((L.m_cap, H), dtype=b.ydt, device=b.dev)
+        rdg.rdg_dispatch(b.x, None, b.DT, ids, L, xp)
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps + 1)]
+        for e3 in ev:
+            e3[0].record()
+            rdg.rdg_grouped_gate_up(L, b.DT, H, I, xp, None, b.W["W1"], b.W["W3"], None, None, h, None)
+            e3[1].record()
+            rdg.rdg_grouped_down(L, b.DT, H, I, h, None, b.W["W2"], None, y)
+            e3[2].record()
+        torch.cuda.synchronize()
+        rows = int(L.masked_m.cpu().sum())
+        g = float(np.mean([e3[0].elapsed_time(e3[1]) for e3 in ev[1:]]))
+        d = float(np.mean([e3[1].elapsed_time(e3[2]) for e3 in ev[1:]]))
+        tiles = int(((L.masked_m.cpu().numpy() + 127) // 128).sum())
+        fg = 4 * rows * H * I / (g * 1e-3) / 1e12
+        fd = 2 * rows * H * I / (d * 1e-3) / 1e12
+        return {"rows": rows, "row_tiles": tiles, "gate_up_ms": g, "gate_up_tflops": fg, "gate_up_mfma_frac": fg / peak,
+                "down_ms": d, "down_tflops": fd, "down_mfma_frac": fd / peak}
+
+    out = {"min_rows": min_rows, "experts": heavy, "together": run(heavy)}
+    out["each"] = {str(e): run([e]) for e in heavy}
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU's share of the layer; runs on several GPUs (--gpus %d) are not "
+              "supported (the expert-parallel sharding is described, not implemented)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo, replicas=args.eplb_replicas)
+    res = measure(b, args, args.steps, args.warmup, args.workload)
+    line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": res["config"],
+            "roofline": res["roofline"], "layer": res["layer"]}
+    if b.rank and b.signals is not None:
+        line["sbo"] = sbo_compare(b, args.steps)
+    if not b.rank and b.cfg["layout"] == "contiguous" and b.cfg["H"] >= 1024 and not args.tbo:
+        line["heavy_experts"] = heavy_experts(b)
+    n_cpu = CPU_TOKENS[args.workload] if args.cpu_tokens is None else args.cpu_tokens
+    if n_cpu != 0:
+        line["cpu_baseline"] = cpu_baseline(b, n_cpu)
     if args.calibrate_copy:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -536,41 +670,140 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    summary = args.summary == "on" or (args.summary == "auto" and args.workload == DEFAULT_WORKLOAD and
+                                       not (args.graph or args.tbo or args.ue8m0 or args.eplb_replicas))
+    del b
+    torch.cuda.empty_cache()
+    if summary:
+        line["workloads"] = summarise([w for w in ALL_WORKLOADS if w != args.workload], args)
     print(json.dumps(line), flush=True)
 
 
-def cpu_baseline(b, n_tok):
-    """The CPU oracle, as it stands, on the same workload: routing of the whole
-    batch, the layout, and the layer output of the first n_tok tokens (by
-    default all of them: about 8 s on 16 cores).  Host copies of the needed inputs (from the generator) are
-    made before the clock starts."""
+def summarise(names, args):
+    """Every other workload measured in this run (10 timed steps each) with
+    its own roofline, layer fraction, CPU-oracle baseline on a small sample,
+    and for the prefill rank share its overlap comparison."""
+    import torch
+    out = {}
+    for name in names:
+        try:
+            b = Bench(name, "cuda:0")
+            r = measure(b, args, 10, 3, name)
+            entry = {"value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"], "dtype": r["dtype"],
+                     "roofline": {k: r["roofline"][k] for k in ("bound", "frac", "achieved", "unit", "avg_ms",
+                                                                "hbm_frac", "mfma_frac")},
+                     "layer_frac": r["layer"]["frac"],
+                     "config": {k: r["config"][k] for k in ("tokens", "routed_rows", "active_experts",
+                                                            "load_balance_mean_over_max") if k in r["config"]}}
+            if b.rank:
+                entry["config"]["rows_per_local_expert"] = r["config"]["rows_per_local_expert"]
+                entry["config"]["eplb_replicas"] = r["config"]["eplb_replicas"]
+            if b.rank and b.signals is not None:
+                entry["sbo"] = sbo_compare(b, 10, rounds=3)
+            n_cpu = SUMMARY_CPU_TOKENS.get(name, 0)
+            if n_cpu != 0:
+                entry["cpu_baseline"] = cpu_baseline(b, n_cpu)
+                if name == "tiny_fp32":
+                    import oracle
+                    prev = oracle.set_num_threads(1)
+                    try:
+                        entry["cpu_baseline_1_thread"] = cpu_baseline(b, n_cpu)
+                    finally:
+                        oracle.set_num_threads(prev)
+            out[name] = entry
+            del b
+        except Exception as ex:  # one workload's failure is reported, not fatal to the line
+            out[name] = {"error": "%s: %s" % (type(ex).__name__, ex)}
+        torch.cuda.empty_cache()
+        print("measured %s" % name, file=sys.stderr, flush=True)
+    return out
+
+
+def _u16(t):
     import numpy as np
     import torch
+    return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline(b, n_tok):
+    """The CPU oracle, as it stands, on the same workload.  Routing (or the
+    rank share's replica remap) and the layout cover the whole batch; the
+    layer output (routed experts + shared expert) is computed for the first
+    n_tok tokens (-1: all of them).  The rate is scaled to the whole batch:
+    time per token = routing-and-layout time / tokens + FFN time / sampled
+    tokens (rank shares: per received row, reported as rows / K).  Host
+    copies of the inputs (from the generator) are made before the clock."""
+    import numpy as np
 
     import oracle
     cfg, synth = b.cfg, b.synth
-
-    def u16(t):
-        return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
-
-    ri, _ = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
-    sel = np.arange(n_tok, dtype=np.int32)
+    K, N = cfg["K"], cfg["N"]
+    fp8 = b.fp8
+    dt = {"f32": oracle.F32, "bf16": oracle.BF16, "fp8": oracle.FP8}[cfg["dtype"]]
+    if b.ue8m0:
+        dt = oracle.FP8_UE8M0
+    if b.rank:
+        ids = b.ids.cpu().numpy()
+        gidx = b.gidx.cpu().numpy()
+        w = b.tw.cpu().numpy()
+        plan = b.plan
+        T = ids.shape[0]
+        n = T if n_tok < 0 else min(n_tok, T)
+        loc = oracle.eplb_remap(ids, gidx, plan["log2phy"], plan["n_replica"], plan["phys_begin"], plan["n_local"])
+        sel = np.arange(n, dtype=np.int32)
+        local_logical = b.local_logical
+        xb = synth.x(cfg, T, device=b.dev)
+        xq, xs = oracle.quantize_fp8(_u16(xb), 1, ue8m0=b.ue8m0)
+        experts = []
+        for e in local_logical:
+            wt = synth.expert_weights(cfg, e, device=b.dev)
+            ex = {}
+            for k, key in (("W1", "1"), ("W3", "3"), ("W2", "2")):
+                q, s = oracle.quantize_fp8(wt[k].cpu().numpy(), 128, ue8m0=b.ue8m0)
+                ex["W" + key], ex["s" + key] = q, s
+            experts.append(ex)
+        rows_total = int((loc >= 0).sum())
+        rows_sample = int((loc[:n] >= 0).sum())
+        t0 = time.perf_counter()
+        loc2 = oracle.eplb_remap(ids, gidx, plan["log2phy"], plan["n_replica"], plan["phys_begin"], plan["n_local"])
+        kind = oracle.MASKED if cfg["layout"] == "masked" else oracle.CONTIGUOUS
+        oracle.layout(loc2, plan["n_local"], kind, block_m=128, m_max=cfg.get("m_max", 0))
+        t1 = time.perf_counter()
+        oracle.moe_layer(dt, xq, loc2, w, experts, x_scales=xs, sel=sel)
+        t2 = time.perf_counter()
+        per_row = (t1 - t0) / rows_total + (t2 - t1) / max(rows_sample, 1)
+        return {"value": 1.0 / per_row / K, "unit": "token-equivalents/s", "cores": oracle.num_threads(),
+                "kind": "oracle", "seconds": t2 - t0,
+                "sample": "replica remap and layout of all %d received rows; the fp64 layer output of the first %d "
+                          "tokens (%d rows); rate per received row scaled to the whole share" %
+                          (rows_total, n, rows_sample)}
+    B = b.logits_np.shape[0]
+    n = B if n_tok < 0 else min(n_tok, B)
+    ri, _ = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], K, cfg["scale"])
+    sel = np.arange(n, dtype=np.int32)
     used = set(np.unique(ri[sel]).tolist())
-    experts = [{k: u16(v) for k, v in synth.expert_weights(cfg, e, device=b.dev).items()} if e in used else None
-               for e in range(cfg["N"])]
-    shared = {k: u16(v) for k, v in synth.expert_weights(cfg, 0, device=b.dev, shared=True).items()}
-    xh = u16(b.x)
+    if cfg["dtype"] == "f32":
+        conv = lambda t: t.detach().cpu().numpy()
+    else:
+        conv = _u16
+    experts = [{k: conv(v) for k, v in synth.expert_weights(cfg, e, device=b.dev).items()} if e in used else None
+               for e in range(N)]
+    shared = {k: conv(v) for k, v in synth.expert_weights(cfg, 0, device=b.dev, shared=True).items()}
+    xh = conv(b.x)
+    kind = oracle.MASKED if cfg["layout"] == "masked" else oracle.CONTIGUOUS
     t0 = time.perf_counter()
-    ids, w = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
-    oracle.layout(ids, cfg["N"], oracle.MASKED, m_max=cfg["m_max"])
-    oracle.moe_layer(oracle.BF16, xh, ids, w, experts, shared=shared, sel=sel)
-    dt = time.perf_counter() - t0
-    return {"value": n_tok / dt, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "seconds": dt,
-            "sample": ("the whole batch: routing, layout and the fp64 layer output (8 routed experts + shared) "
-                       "of all %d tokens" % n_tok) if n_tok == b.logits_np.shape[0] else
-                      ("route all %d tokens, layout, and the fp64 layer output (8 routed experts + shared) of "
-                       "the first %d tokens" % (b.logits_np.shape[0], n_tok))}
+    ids, w = oracle.route(b.logits_np, cfg["n_group"], cfg["topk_group"], K, cfg["scale"])
+    oracle.layout(ids, N, kind, block_m=128, m_max=cfg.get("m_max", 0))
+    t1 = time.perf_counter()
+    oracle.moe_layer(dt, xh, ids, w, experts, shared=shared, sel=sel)
+    t2 = time.perf_counter()
+    per_tok = (t1 - t0) / B + (t2 - t1) / n
+    return {"value": 1.0 / per_tok, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "seconds": t2 - t0,
+            "sample": ("the whole batch: routing, layout and the fp64 layer output (%d routed experts + shared) "
+                       "of all %d tokens" % (K, n)) if n == B else
+                      ("routing and layout of all %d tokens; the fp64 layer output (%d routed experts + shared) of "
+                       "the first %d; rate per token scaled to the whole batch" % (B, K, n))}
 
 
 if __name__ == "__main__":

@@ -1,6 +1,7 @@
 """bench.py's command line on the CPU: more than one GPU is refused with exit
 code 2 before anything touches a device, and the defaults are one GPU, the
-decode layer and a run of 5 + 20 steps."""
+4096-token prefill layer (the largest configuration on one GPU), a run of
+5 + 20 steps, and the summary of every other workload."""
 import os
 import subprocess
 import sys
@@ -21,8 +22,10 @@ def test_defaults(monkeypatch):
     import bench
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = bench.parse()
-    assert (a.gpus, a.steps, a.warmup, a.workload, a.cpu_tokens) == (1, 20, 5, "decode_bf16", -1)
+    assert (a.gpus, a.steps, a.warmup, a.workload, a.cpu_tokens) == (1, 20, 5, "prefill_bf16", None)
+    assert a.summary == "auto" and a.eplb_replicas is None
     assert not (a.graph or a.ue8m0 or a.tbo or a.calibrate_copy)
+    assert bench.CPU_TOKENS["prefill_bf16"] > 0 and set(bench.CPU_TOKENS) == set(bench.ALL_WORKLOADS)
 
 
 def test_layer_bytes_decode():

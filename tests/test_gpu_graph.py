@@ -9,12 +9,16 @@ torch.cuda.graph.  Between replays the program does its own eager work: new
 router logits and tokens are copied into the captured input buffers, the
 same step runs eagerly on them, and the output buffer is poisoned with NaN.
 Every replay must then reproduce the eager output bit for bit (all the
-kernels are deterministic)."""
+kernels are deterministic), and the last replay's output must equal the
+oracle's definition of the layer on every token (max|out-ref|/max|ref| <=
+2e-2, bf16)."""
+import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
-from harness import DEV, ExpertSet, rdg
+from harness import DEV, ExpertSet, check_rows, np_of, out_as_f64, rdg
 
 pytestmark = pytest.mark.gpu
 
@@ -43,8 +47,17 @@ class DecodeStep:
 
     def load_inputs(self, index):
         cfg = dict(self.cfg, wid=self.cfg["wid"] + 1000 * index)
-        self.logits.copy_(torch.from_numpy(synth.logits(cfg, self.B)))
+        self.logits_np = synth.logits(cfg, self.B)
+        self.logits.copy_(torch.from_numpy(self.logits_np))
         self.x.copy_(synth.x(cfg, self.B, device=DEV))
+
+    def oracle_out(self):
+        """The layer on the current inputs by the oracle's definition (bf16 bits)."""
+        cfg = self.cfg
+        ri, rw = oracle.route(self.logits_np, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
+        used = set(np.unique(ri).tolist())
+        experts = [self.experts.oracle_expert(j) if j in used else None for j in range(cfg["N"])]
+        return oracle.moe_layer(oracle.BF16, np_of(self.x), ri, rw, experts, shared=self.shared.oracle_expert(0))
 
     def __call__(self):
         m, cfg, B = self.m, self.cfg, self.B
@@ -94,3 +107,9 @@ def test_graph_replay_matches_eager(name):
         assert not torch.isnan(step.out.float()).any(), "replay %d left poisoned output" % rep
         assert torch.equal(got, ref.view(torch.int16)), "replay %d differs from the eager step" % rep
         print("%s replay %d bit-equal to eager" % (name, rep), flush=True)
+    want = step.oracle_out()
+    out = np_of(step.out)
+    err = oracle.rel_err(out_as_f64(out), out_as_f64(want))
+    row = check_rows(out, want, dict(cfg, dtype="bf16"), "graph replay")
+    print("%s last replay against the oracle: rel_err=%.3e worst token %.3e" % (name, err, row), flush=True)
+    assert err <= 2e-2

@@ -41,6 +41,29 @@ def _sample(T, n, seed):
     return np.unique(np.concatenate([np.arange(8), mid, np.arange(T - 8, T)]))
 
 
+def _cover(ids, n_local, n, seed, tile=128):
+    """Tokens to compare at full size: for every expert with rows, the
+    tokens of its first row, of its last row and of the first row of each of
+    its 128-row tiles (rows are stable by flat index t*K+k, so an expert's
+    j-th row belongs to its j-th token in index order), then seeded random
+    tokens up to n."""
+    T = ids.shape[0]
+    flat = ids.ravel()
+    keep = set()
+    for e in range(n_local):
+        toks = np.flatnonzero(flat == e) // ids.shape[1]
+        if len(toks) == 0:
+            continue
+        keep.update(toks[::tile].tolist())
+        keep.add(int(toks[-1]))
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.array(sorted(keep), dtype=np.int64))
+    extra = max(0, n - len(keep))
+    if extra:
+        keep.update(rng.choice(rest, size=min(extra, len(rest)), replace=False).tolist())
+    return np.array(sorted(keep), dtype=np.int64)
+
+
 def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
     """Workloads where this GPU holds every expert (the tiny, decode and prefill layers)."""
     m = rdg()
@@ -66,7 +89,8 @@ def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
     ref_l = oracle.layout(ri, N, kind, block_m=block_m, m_max=m_max)
     assert st == (ref_l["status"], ref_l["detail"])
     check_layout(r["L"], ref_l, ri.shape)
-    sel = _sample(B, n_sample, seed) if n_sample else np.arange(B)
+    sel = _cover(ri, N, n_sample, seed) if n_sample else np.arange(B)
+    print("%s comparing %d of %d tokens with the oracle" % (cfg.get("name", ""), len(sel), B), flush=True)
     used = set(np.unique(ri[sel]).tolist())
     ref = oracle.moe_layer(dt, xo, ri, rw, _oracle_experts(experts, used),
                            shared=shared.oracle_expert(0) if shared else None, x_scales=xo_s, sel=sel)
@@ -128,19 +152,19 @@ def test_tiny_fp32_workload():
 
 def test_decode_bf16_workload():
     cfg = dict(synth.WORKLOADS["decode_bf16"], name="decode_bf16")
-    _full_layer(cfg, cfg["B"], rdg().RDG_MASKED, m_max=cfg["m_max"], n_sample=24, seed=2)
+    _full_layer(cfg, cfg["B"], rdg().RDG_MASKED, m_max=cfg["m_max"])   # every token
 
 
 def test_prefill_bf16_workload():
     cfg = dict(synth.WORKLOADS["prefill_bf16"], name="prefill_bf16")
-    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=32, seed=3)
+    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=256, seed=3)
 
 
 def test_prefill_bf16_balanced_workload():
     # the "simulated perfect EPLB" distribution of the H100 deployment
     # article's prefill evaluation: random group-limited choices
     cfg = dict(synth.WORKLOADS["prefill_bf16_balanced"], name="prefill_bf16_balanced")
-    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=32, seed=4)
+    _full_layer(cfg, cfg["B"], rdg().RDG_CONTIGUOUS, block_m=128, n_sample=256, seed=4)
 
 
 # ---------------------------------------------------------------- rank shares
@@ -174,7 +198,7 @@ def rank_share(cfg):
                 rows=taken, local_logical=local_logical, w_dev=w[torch.from_numpy(toks).to(DEV)].contiguous())
 
 
-def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False, n_sample=32, seed=0):
+def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False, n_sample=256, seed=0):
     m = rdg()
     share = rank_share(cfg)
     assert share["rows"] == cfg["rows"]
@@ -200,7 +224,8 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
     ref_l = oracle.layout(rloc, plan["n_local"], kind, block_m=block_m, m_max=m_max)
     assert st == (ref_l["status"], ref_l["detail"])
     check_layout(r["L"], ref_l, rloc.shape)
-    sel = _sample(T, n_sample, seed)
+    sel = _cover(rloc, plan["n_local"], n_sample, seed) if n_sample else np.arange(T)
+    print("%s comparing %d of %d tokens with the oracle" % (cfg["name"], len(sel), T), flush=True)
     oe = [experts.oracle_expert(j) for j in range(plan["n_local"])]
     ref = oracle.moe_layer(dt_code(cfg), rq, rloc, share["w"], oe, x_scales=rs, sel=sel)
     got = np_of(r["out"])[sel]
@@ -231,7 +256,7 @@ def _rank_layer(cfg, kind, m_max=0, block_m=128, signals=False, concurrent=False
 
 def test_decode_rank_fp8_workload():
     cfg = dict(synth.WORKLOADS["decode_rank_fp8"], name="decode_rank_fp8")
-    _rank_layer(cfg, rdg().RDG_MASKED, m_max=cfg["m_max"])
+    _rank_layer(cfg, rdg().RDG_MASKED, m_max=cfg["m_max"], n_sample=None)   # every token
 
 
 @pytest.mark.parametrize("name", ["decode_rank_fp8", "prefill_rank_fp8"])
