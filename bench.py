@@ -349,6 +349,13 @@ class Bench:
         self.nrep = torch.from_numpy(plan["n_replica"]).to(self.dev)
         gidx = torch.arange(Tg, dtype=torch.int64, device=self.dev)
         loc = torch.empty_like(gids)
+        # the measured rank: the one that receives the most rows of the global batch
+        rows = []
+        for r in range(cfg["n_ranks"]):
+            rdg.rdg_eplb_remap(gids, gidx, self.l2p, self.nrep, r * plan["n_local"], plan["n_local"], loc)
+            rows.append(int((loc >= 0).sum()))
+        self.plan = plan = synth.measured_rank(plan, rows)
+        self.rank_rows = rows
         rdg.rdg_eplb_remap(gids, gidx, self.l2p, self.nrep, plan["phys_begin"], plan["n_local"], loc)
         loc_np = loc.cpu().numpy()
         toks, keep = synth.take_rank_rows(loc_np, cfg["rows"])
@@ -567,7 +574,9 @@ def measure(b, args, steps, warmup, workload):
         conf["m_max"] = cfg["m_max"]
     if b.rank:
         conf.update(local_experts=cfg["n_local"], ranks=cfg["n_ranks"], received_rows=rows,
-                    eplb_replicas=b.plan["rule"], rows_per_local_expert=b.L.masked_m.cpu().tolist())
+                    eplb_replicas=b.plan["rule"], measured_rank=b.plan["rank"],
+                    rank_rows_max_over_mean=round(max(b.rank_rows) * len(b.rank_rows) / sum(b.rank_rows), 4),
+                    rows_per_local_expert=b.L.masked_m.cpu().tolist())
     lb = layer_bytes(cfg, b.T, rows, active, esz)
     layer = {"algorithmic_bytes": lb, "achieved": lb / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}

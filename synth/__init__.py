@@ -27,11 +27,12 @@ Five workloads, named by what they are:
                      each given greedily to the expert with the largest
                      expected load per copy; ``replicas="one_each"`` gives
                      the 32 most popular experts one extra copy each
-                     instead), the bottleneck rank receives 1024
+                     instead); the rank that receives the most rows of the
+                     global batch (the bottleneck) takes its first 1024
                      token-expert rows; fp8 e4m3 with 1x128 / 128x128 block
                      scales; masked layout.
 * ``prefill_rank_fp8`` one prefill rank's share: 32 ranks x 9 physical
-                     experts, 16384 received rows, shared expert on the
+                     experts, the bottleneck rank's first 16384 received rows, shared expert on the
                      rank's own 2048 tokens; fp8; contiguous layout; the
                      down projection signals a concurrently running combine.
 
@@ -201,7 +202,9 @@ def eplb_plan(cfg, rule=None):
     to the least-loaded rank that still has a free slot (ties: lower rank).
     Physical id = rank * n_local + slot.  Returns log2phy [N, r_max] (unused
     columns repeat the first copy), n_replica [N], the expected rank loads,
-    and the bottleneck rank (highest expected load, ties lower rank).
+    and the rank with the highest expected load (ties lower rank) as a first
+    choice of the measured rank; measured_rank replaces it by the rank that
+    receives the most rows once the global batch has been routed.
     """
     N, n_ranks, n_local = cfg["N"], cfg["n_ranks"], cfg["n_local"]
     assert n_ranks * n_local == N + cfg["n_redundant"]
@@ -225,6 +228,16 @@ def eplb_plan(cfg, rule=None):
     bottleneck = int(np.argmax(load))
     return dict(log2phy=log2phy, n_replica=n_rep, load=load, bottleneck=bottleneck,
                 phys_begin=bottleneck * n_local, n_local=n_local, rule=rule)
+
+
+def measured_rank(plan, rows_per_rank):
+    """The rank whose share is measured: the one that receives the most
+    rows of the routed global batch (the bottleneck of an expert-parallel
+    step; ties: lower rank).  rows_per_rank comes from the caller's routing
+    and replica remap of the global batch.  Returns the plan with that
+    rank's physical range."""
+    r = int(np.argmax(np.asarray(rows_per_rank)))
+    return dict(plan, rank=r, phys_begin=r * plan["n_local"])
 
 
 def take_rank_rows(local_ids, rows):

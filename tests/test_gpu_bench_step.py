@@ -93,6 +93,9 @@ def _rank_reference(b, sel):
     lg = synth.logits(cfg)
     ri, rw = oracle.route(lg, cfg["n_group"], cfg["topk_group"], cfg["K"], cfg["scale"])
     gidx = np.arange(ri.shape[0], dtype=np.int64)
+    rows = [int((oracle.eplb_remap(ri, gidx, plan["log2phy"], plan["n_replica"], r * plan["n_local"],
+                                   plan["n_local"]) >= 0).sum()) for r in range(cfg["n_ranks"])]
+    assert int(np.argmax(rows)) == plan["rank"], "measured rank differs from the oracle's choice"
     rloc = oracle.eplb_remap(ri, gidx, plan["log2phy"], plan["n_replica"], plan["phys_begin"], plan["n_local"])
     toks, keep = synth.take_rank_rows(rloc, cfg["rows"])
     ids = ri[toks].copy()
@@ -139,6 +142,7 @@ def test_bench_step_rank_shares(name, ue8m0, replicas):
     n = None if name == "decode_rank_fp8" else 256
     T = b.T
     ids = np_of(b.local)
+    assert int((ids >= 0).sum()) == b.cfg["rows"], "the share must hold exactly the configured rows"
     sel = np.arange(T) if n is None else _cover(ids, b.cfg["n_local"], n, 9)
     print("%s: comparing %d of %d tokens" % (name, len(sel), T), flush=True)
     ref, _ = _rank_reference(b, sel)

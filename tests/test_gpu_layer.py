@@ -170,7 +170,7 @@ def test_prefill_bf16_balanced_workload():
 # ---------------------------------------------------------------- rank shares
 def rank_share(cfg):
     """One rank's received tokens under the EPLB placement: route the global
-    batch (checked bit-exact), remap onto the bottleneck rank, and take the
+    batch (checked bit-exact), remap onto the rank that receives the most rows, and take the
     tokens that send it rows, in global order, until exactly cfg['rows'] rows
     (the last token's surplus local rows are marked -1: not sent)."""
     m = rdg()
@@ -180,6 +180,9 @@ def rank_share(cfg):
     Tg, K = ri.shape
     gidx = np.arange(Tg, dtype=np.int64)
     l2p, nrep = plan["log2phy"], plan["n_replica"]
+    rows = [int((oracle.eplb_remap(ri, gidx, l2p, nrep, r * plan["n_local"], plan["n_local"]) >= 0).sum())
+            for r in range(cfg["n_ranks"])]
+    plan = synth.measured_rank(plan, rows)
     loc = torch.empty((Tg, K), dtype=torch.int32, device=DEV)
     m.rdg_eplb_remap(ids, torch.from_numpy(gidx).to(DEV), torch.from_numpy(l2p).to(DEV),
                      torch.from_numpy(nrep).to(DEV), plan["phys_begin"], plan["n_local"], loc)
