@@ -205,6 +205,24 @@ size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);
 int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
                  const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream);
 
+/* Allocation-free dispatch, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Computes exactly what rdg_dispatch computes; its scratch
+ * (per-chunk expert counts and one rank per dispatched entry) lives in a
+ * static device array inside the library, 4.25 MiB per GPU, held until the
+ * process ends, instead of in a caller workspace.  L->work then needs only
+ * the layout's row-tile tables, rdg_layout_tables_bytes(L->n_local) bytes,
+ * which the grouped GEMMs read later.  At most 2^20 dispatched entries
+ * (T * K); more returns RDG_EUNSUPPORTED and enqueues nothing.  Every call
+ * on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or on one stream under concurrent graph replays) race,
+ * so serialise them.  Nothing in the array needs clearing between calls.
+ * No allocating call is made (the array's device address is looked up once
+ * per device on the first call). */
+size_t rdg_layout_tables_bytes(int n_local);
+int rdg_dispatch_noalloc(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
+                         const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream);
+
 /* Describe T rows as one expert's segment (rows [0, T)), for running a dense
  * FFN -- the shared expert -- through rdg_grouped_ffn with n_local = 1.
  * Writes counts, offsets, masked_m and the work area; L->kind must be

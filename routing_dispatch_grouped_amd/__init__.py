@@ -46,6 +46,8 @@ _SIGS = {
     "rdg_tbo_split": ([_P, _I, _I], _I),
     "rdg_dispatch_workspace_bytes": ([_I, _I, _I], _SZ),
     "rdg_dispatch": ([_P, _P, _I, _I, _I, _P, _I, _LP, _P, _P, _P], _I),
+    "rdg_dispatch_noalloc": ([_P, _P, _I, _I, _I, _P, _I, _LP, _P, _P, _P], _I),
+    "rdg_layout_tables_bytes": ([_I], _SZ),
     "rdg_layout_dense": ([_I, _LP, _P], _I),
     "rdg_grouped_ffn": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_grouped_gate_up": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
@@ -182,6 +184,19 @@ def rdg_dispatch(x, x_scales, dtype, ids, layout, x_perm, x_perm_scales=None, st
     K = ids.shape[1]
     _check(_lib.rdg_dispatch(_ptr(x), _ptr(x_scales), dtype, T, H, _ptr(ids), K, layout.ref, _ptr(x_perm),
                              _ptr(x_perm_scales), _stream(stream)), "rdg_dispatch")
+
+
+def rdg_layout_tables_bytes(n_local):
+    return int(_lib.rdg_layout_tables_bytes(n_local))
+
+
+def rdg_dispatch_noalloc(x, x_scales, dtype, ids, layout, x_perm, x_perm_scales=None, stream=None):
+    """rdg_dispatch with its scratch in the library's static device array
+    (layout.work then needs only rdg_layout_tables_bytes(n_local) bytes)."""
+    T, H = x.shape
+    K = ids.shape[1]
+    _check(_lib.rdg_dispatch_noalloc(_ptr(x), _ptr(x_scales), dtype, T, H, _ptr(ids), K, layout.ref, _ptr(x_perm),
+                                     _ptr(x_perm_scales), _stream(stream)), "rdg_dispatch_noalloc")
 
 
 def rdg_layout_dense(T, layout, stream=None):

@@ -121,11 +121,13 @@ size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local) {
     return ws_tile_off_bytes(n_local) + ws_chunk_bytes(n_local) + align256(sizeof(int32_t) * (size_t)T * K);
 }
 
-int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
-                 const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream) {
-    if (!layout_ok(L) || T < 0 || K < 1 || K > 32 || H < 16 || H % 16 != 0) return RDG_EINVAL;
-    if ((int64_t)T * K != L->n_rows) return RDG_EINVAL;
-    if (!L->pos || !L->row_src || !L->status) return RDG_EINVAL;
+// Argument checks shared by both dispatch entry points; the element size on
+// success (0 on an invalid argument).
+static int dispatch_esz(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
+                        const rdg_layout* L, void* x_perm, float* x_perm_scales) {
+    if (!layout_ok(L) || T < 0 || K < 1 || K > 32 || H < 16 || H % 16 != 0) return 0;
+    if ((int64_t)T * K != L->n_rows) return 0;
+    if (!L->pos || !L->row_src || !L->status) return 0;
     int esz;
     switch (dtype) {
         case RDG_F32: esz = 4; break;
@@ -133,12 +135,33 @@ int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, 
         case RDG_FP8_E4M3:
         case RDG_FP8_E4M3_UE8M0:
             esz = 1;
-            if (H % 128 != 0) return RDG_EINVAL;
-            if (T > 0 && (!x_scales || !x_perm_scales)) return RDG_EINVAL;
+            if (H % 128 != 0) return 0;
+            if (T > 0 && (!x_scales || !x_perm_scales)) return 0;
             break;
-        default: return RDG_EINVAL;
+        default: return 0;
     }
-    if (T > 0 && (!x || !ids || !x_perm || !aligned16(x) || !aligned16(x_perm))) return RDG_EINVAL;
+    if (T > 0 && (!x || !ids || !x_perm || !aligned16(x) || !aligned16(x_perm))) return 0;
+    return esz;
+}
+
+size_t rdg_layout_tables_bytes(int n_local) {
+    if (n_local < 1) return 0;
+    return ws_tile_off_bytes(n_local);
+}
+
+int rdg_dispatch_noalloc(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
+                         const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream) {
+    const int esz = dispatch_esz(x, x_scales, dtype, T, H, ids, K, L, x_perm, x_perm_scales);
+    if (esz == 0) return RDG_EINVAL;
+    if ((int64_t)T * K > kNoallocMaxEntries) return RDG_EUNSUPPORTED;
+    return hip_rc(launch_dispatch_noalloc(x, esz == 1 ? x_scales : nullptr, H * esz, T, H, ids, K, *L, x_perm,
+                                          x_perm_scales, stream));
+}
+
+int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
+                 const rdg_layout* L, void* x_perm, float* x_perm_scales, rdg_stream_t stream) {
+    const int esz = dispatch_esz(x, x_scales, dtype, T, H, ids, K, L, x_perm, x_perm_scales);
+    if (esz == 0) return RDG_EINVAL;
     return hip_rc(launch_dispatch(x, esz == 1 ? x_scales : nullptr, H * esz, T, H, ids, K, *L, x_perm,
                                   x_perm_scales, stream));
 }

@@ -22,6 +22,8 @@
 //               destinations and copies the slice once from HBM into each of
 //               them (16-byte vectors); slicing keeps small batches from
 //               leaving most CUs idle.
+#include <mutex>
+
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -317,15 +319,18 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, int T, int H, const int32_t* ids,
-                           int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s) {
+// The three passes.  tile_off: the layout's row-tile tables (an output the
+// grouped GEMMs read); chunk_counts [kMaxChunks x n_local] and tmp_rank [T*K]:
+// scratch, every element read written first by the same dispatch (k_rank
+// writes each used chunk's counts and each routed entry's rank; k_scan and
+// k_scatter read only those), so nothing needs clearing between calls.
+static hipError_t dispatch_passes(const void* x, const float* x_scales, int row_bytes, int T, int H,
+                                  const int32_t* ids, int K, const rdg_layout& L, void* x_perm,
+                                  float* x_perm_scales, int32_t* tile_off, int32_t* chunk_counts, int32_t* tmp_rank,
+                                  hipStream_t s) {
     const int64_t n = (int64_t)T * K;
     const int chunk = chunk_size_for(n);
     const int n_chunks = n > 0 ? (int)((n + chunk - 1) / chunk) : 0;
-    uint8_t* ws = static_cast<uint8_t*>(L.work);
-    int32_t* tile_off = reinterpret_cast<int32_t*>(ws);
-    int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local));
-    int32_t* tmp_rank = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local) + ws_chunk_bytes(L.n_local));
     int nbits = 1;
     while ((1 << nbits) < L.n_local + 1) ++nbits;
 
@@ -351,6 +356,64 @@ hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, 
                                                           tmp_rank, L.offsets, L.masked_m, L.pos, L.row_src,
                                                           static_cast<uint8_t*>(x_perm), x_perm_scales);
     return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, int T, int H, const int32_t* ids,
+                           int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s) {
+    uint8_t* ws = static_cast<uint8_t*>(L.work);
+    int32_t* tile_off = reinterpret_cast<int32_t*>(ws);
+    int32_t* chunk_counts = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local));
+    int32_t* tmp_rank = reinterpret_cast<int32_t*>(ws + ws_tile_off_bytes(L.n_local) + ws_chunk_bytes(L.n_local));
+    return dispatch_passes(x, x_scales, row_bytes, T, H, ids, K, L, x_perm, x_perm_scales, tile_off, chunk_counts,
+                           tmp_rank, s);
+}
+
+// ---------------------------------------------------------------- no allocation
+// The allocation-free dispatch keeps its scratch (per-chunk counts for up to
+// kMaxChunks x 1024 experts, one rank per dispatched entry for up to
+// kNoallocMaxEntries entries) in this file-scope device array: 4.25 MiB,
+// held by every GPU the library runs on until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it is a stand-in,
+// not a device address): the device address comes from hipGetSymbolAddress,
+// once per device, with that device current.
+namespace {
+constexpr size_t kNoallocChunkBytes = sizeof(int32_t) * kMaxChunks * 1024;
+constexpr size_t kScratchBytes = kNoallocChunkBytes + sizeof(int32_t) * (size_t)kNoallocMaxEntries;
+static_assert(kNoallocChunkBytes % 256 == 0, "rank area aligned");
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_dispatch_noalloc(const void* x, const float* x_scales, int row_bytes, int T, int H,
+                                   const int32_t* ids, int K, const rdg_layout& L, void* x_perm, float* x_perm_scales,
+                                   hipStream_t s) {
+    void* base = nullptr;
+    hipError_t e = scratch_address(&base);
+    if (e != hipSuccess) return e;
+    int32_t* chunk_counts = static_cast<int32_t*>(base);
+    int32_t* tmp_rank = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(base) + kNoallocChunkBytes);
+    return dispatch_passes(x, x_scales, row_bytes, T, H, ids, K, L, x_perm, x_perm_scales,
+                           static_cast<int32_t*>(L.work), chunk_counts, tmp_rank, s);
 }
 
 hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s) {

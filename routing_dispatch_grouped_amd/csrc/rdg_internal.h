@@ -132,6 +132,12 @@ hipError_t launch_remap(const int32_t* ids, const int64_t* gidx, int T, int K, c
                         int32_t* out, hipStream_t s);
 hipError_t launch_dispatch(const void* x, const float* x_scales, int row_bytes, int T, int H, const int32_t* ids,
                            int K, const rdg_layout& L, void* x_perm, float* x_perm_scales, hipStream_t s);
+// The same with the scratch in the library's static device array; L.work
+// holds only the row-tile tables.  At most kNoallocMaxEntries entries.
+constexpr int64_t kNoallocMaxEntries = 1 << 20;
+hipError_t launch_dispatch_noalloc(const void* x, const float* x_scales, int row_bytes, int T, int H,
+                                   const int32_t* ids, int K, const rdg_layout& L, void* x_perm, float* x_perm_scales,
+                                   hipStream_t s);
 hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 hipError_t launch_pack(const void* W, int dtype, int n_mat, int rows, int cols, void* P, hipStream_t s);
