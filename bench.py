@@ -383,6 +383,7 @@ class Bench:
             self.signal_rows = rows
             self.signals = torch.zeros(((self.L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=self.dev)
             self.threshold = rdg.rdg_signal_threshold(cfg["H"], self.DT)
+            self.poll_blocks = 64  # the polling combine's workgroups (the library caps them at a quarter of the CUs)
             self.side = torch.cuda.Stream()
             self.gate_done = torch.cuda.Event()
         if cfg.get("shared_I"):
@@ -469,7 +470,7 @@ class Bench:
             self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             self.side.wait_event(self.gate_done)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
-                            self.signal_rows, self.threshold, 1_000_000, 64, stream=self.side)
+                            self.signal_rows, self.threshold, 1_000_000, self.poll_blocks, stream=self.side)
         self.stream.wait_stream(self.side)
 
 
@@ -667,6 +668,7 @@ def main():
             "roofline": res["roofline"], "layer": res["layer"]}
     if b.rank and b.signals is not None:
         line["sbo"] = sbo_compare(b, args.steps)
+        line["sbo"]["polling_workgroups"] = b.poll_blocks
     if not b.rank and b.cfg["layout"] == "contiguous" and b.cfg["H"] >= 1024 and not args.tbo:
         line["heavy_experts"] = heavy_experts(b)
     n_cpu = CPU_TOKENS[args.workload] if args.cpu_tokens is None else args.cpu_tokens
@@ -709,6 +711,7 @@ def summarise(names, args):
                 entry["config"]["eplb_replicas"] = r["config"]["eplb_replicas"]
             if b.rank and b.signals is not None:
                 entry["sbo"] = sbo_compare(b, 10, rounds=3)
+                entry["sbo"]["polling_workgroups"] = b.poll_blocks
             n_cpu = SUMMARY_CPU_TOKENS.get(name, 0)
             if n_cpu != 0:
                 entry["cpu_baseline"] = cpu_baseline(b, n_cpu)

@@ -297,6 +297,7 @@ int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h
 int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I);
 int rdg_signal_threshold(int H, int dtype);
 
+
 /* Combine ([DEEP] "EP": weighted sum back to the token; [DEEP] "why is
  * combine slower": transfer plus weighted reduction; [DEEP] "limitations":
  * bf16 pre-reduction is imprecise and non-deterministic, so the sum here is
@@ -319,11 +320,10 @@ int rdg_signal_threshold(int H, int dtype);
  *              workgroups hold their CU, and the down GEMM's workgroups must
  *              always find CUs to run on.
  * The polling form may run on another stream concurrently with the down
- * GEMM, which must have been enqueued first.  It visits the tokens in the
- * order their rows become ready -- each token at its last layout row,
- * walking L->row_src in layout order, which is the order the signalled down
- * GEMM completes its row tiles -- and then the tokens with no local row, so
- * L->row_src must be set.  The output does not depend on the visiting order. */
+ * GEMM, which must have been enqueued first.  Each token is combined at its
+ * last layout row (L->row_src must be set), once every row tile it reads is
+ * complete, and the tokens with no local row after them.  The output does
+ * not depend on the visiting order: it equals the plain form bit for bit. */
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
                 const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
                 int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream);

@@ -13,11 +13,16 @@
 // Design for CDNA4: one wave per (token, 512-feature slice); each lane owns
 // 8 consecutive features (a 16-byte bf16 vector), gathers the K expert rows
 // for them, accumulates in fp32 and writes once.  Slicing the row keeps a
-// 128-token decode batch from occupying only a handful of CUs.  In the
-// polling form, tokens are visited in the order their rows become ready (see
-// k_combine), and lane 0 waits (acquire, device scope) on the counter of each
-// row tile the token reads; a bounded wait turns a tile that never completes
-// into a status code instead of a hang.
+// 128-token decode batch from occupying only a handful of CUs.
+//
+// The polling form (k_combine_poll) runs beside the signalled down GEMM on at
+// most a quarter of the CUs.  Each wave takes single layout rows, strided over
+// the whole layout, and combines every token whose last row it is, after lane
+// 0 has waited for the counter of each row tile the token reads; a bounded
+// wait turns a tile that never completes into a status code instead of a
+// hang.  The published rows are staged in LDS by device-scope direct loads,
+// many in flight per wave, so that a wave is not bound by one memory round
+// trip per 512-feature slice.
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -41,33 +46,6 @@ __device__ __forceinline__ void load8(const void* y, size_t row, int H, int v, f
     }
 }
 
-// load8 for rows published by a concurrently running producer on another
-// XCD: device-scope (relaxed atomic) loads, which read past this CU's L1 and
-// any stale line of this XCD's L2 -- so the consumer needs no device-scope
-// acquire, whose L2 invalidation would hurt the producer's workgroups here.
-template <int YDT>
-__device__ __forceinline__ void load8_published(const void* y, size_t row, int H, int v, float* out) {
-    if (YDT == RDG_BF16) {
-        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const uint16_t*>(y) + row * H) + 2 * v;
-        const uint64_t lo = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t hi = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const uint32_t w[4] = {(uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32)};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            out[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-            out[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-        }
-    } else {
-        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const float*>(y) + row * H) + 4 * v;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint64_t q = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            out[2 * i] = __uint_as_float((uint32_t)q);
-            out[2 * i + 1] = __uint_as_float((uint32_t)(q >> 32));
-        }
-    }
-}
-
 template <int ODT>
 __device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const float* acc) {
     if (ODT == RDG_BF16) {
@@ -84,13 +62,12 @@ __device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const 
     }
 }
 
-// Lane 0 waits for a counter; returns false on timeout.
 // Lane 0 waits for a counter; returns false on timeout.  The polls are
-// relaxed device-scope loads (they read L2, where the producer's release
-// lands, without invalidating this CU's L1 on every poll -- which would slow
-// the GEMM waves sharing the CU); the caller issues one acquire fence once
-// every counter it needs is complete.  Exponential back-off (64 cycles up to
-// about 8k) keeps the polling traffic on the counters' few L2 lines low.
+// relaxed device-scope loads: they read past this CU's L1 and any stale line
+// of this XCD's L2, where the producer's release (a write-back of its own L2)
+// is seen, without invalidating anything the GEMM waves sharing the CU rely
+// on.  Exponential back-off (64 cycles up to about 8k) keeps the polling
+// traffic on the counters' few cache lines low.
 __device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_ticks) {
     if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= threshold) return true;
     const uint64_t t0 = wall_clock64();
@@ -103,50 +80,16 @@ __device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_t
     return true;
 }
 
-__device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) v = max(v, __shfl_xor(v, o));
-    return v;
-}
-
-// READY (polling form): tokens are visited in the order their rows become
-// ready -- token t at its last layout row max_k pos[t,k], walking the layout
-// rows in order, which is the order the signalled down GEMM completes its row
-// tiles -- and then the tokens with no row on this GPU.  Otherwise tokens are
-// visited in index order.
-// Token t's slots into this wave's LDS row: positions (-1: no row, or a row
-// whose tile never completed) and weights.  Polling form: lane 0 first waits
-// for the counter of every row tile the token reads.
+// Token t's slots into this wave's LDS row: positions (-1: no row) and
+// weights; the feature loop may leave lanes idle, so it reads them from LDS.
 __device__ __forceinline__ void token_slots(const int32_t* __restrict__ pos, const float* __restrict__ w, int t,
-                                            int K, const int32_t* signals, int rows_per_sig, int threshold,
-                                            uint64_t timeout_ticks, int32_t* status, int* pos_l, float* w_l,
-                                            int lane, int& known_tile) {
+                                            int K, int* pos_l, float* w_l, int lane) {
     int p = -1;
     float wt = 0.0f;
     if (lane < K) {
         p = pos[(size_t)t * K + lane];
         wt = w[(size_t)t * K + lane];
     }
-    if (signals != nullptr) {
-        for (int k = 0; k < K; ++k) {
-            const int pk = __shfl(p, k);
-            if (pk < 0) continue;
-            const int tile = pk / rows_per_sig;
-            if (tile == known_tile) continue;  // confirmed complete for an earlier token
-            int ok = 1;
-            if (lane == 0) {
-                ok = wait_counter(signals + tile, threshold, timeout_ticks) ? 1 : 0;
-                if (!ok) set_status(status, RDG_ETIMEOUT, tile);
-            }
-            ok = __shfl(ok, 0);
-            if (ok) known_tile = tile;
-            else if (lane == k) p = -1;  // skip the incomplete row
-        }
-        // the rows are then read with device-scope loads (load8_published);
-        // this fence only keeps those loads after the polls
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-    }
-    // the feature loop may leave lanes idle: it reads the slots from LDS
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -185,110 +128,125 @@ __device__ __forceinline__ void combine_slice(const void* __restrict__ y, const 
     store8<ODT>(out, (size_t)t, H, v, acc);
 }
 
-// All slices of token t from published rows, G slices at a time with every
-// row load of a group issued before any is used (the device-scope loads go
-// to memory; one at a time would leave the wave waiting on each).
-template <int YDT, int ODT>
-__device__ __forceinline__ void combine_token_published(const void* __restrict__ y, const void* __restrict__ shared_out,
-                                                        void* __restrict__ out, int t, int K, int H, const int* pos_l,
-                                                        const float* w_l, int lane) {
-    constexpr int G = 7;
-    const int nvec = H / 8;
-    for (int v0 = lane; v0 < nvec; v0 += G * kWave) {
-        float acc[G][8];
-#pragma unroll
-        for (int j = 0; j < G; ++j)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[j][i] = 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int pk = pos_l[k];
-            const float wk = w_l[k];
-            if (pk < 0) continue;
-            float yv[G][8];
-#pragma unroll
-            for (int j = 0; j < G; ++j) {
-                const int v = v0 + j * kWave;
-                if (v < nvec) load8_published<YDT>(y, (size_t)pk, H, v, yv[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < G; ++j)
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[j][i] += wk * yv[j][i];
-        }
-#pragma unroll
-        for (int j = 0; j < G; ++j) {
-            const int v = v0 + j * kWave;
-            if (v >= nvec) continue;
-            if (shared_out != nullptr) {
-                float sv[8];
-                load8<ODT>(shared_out, (size_t)t, H, v, sv);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc[j][i] += sv[i];
-            }
-            store8<ODT>(out, (size_t)t, H, v, acc[j]);
-        }
-    }
-}
-
 // Plain form: one wave per (token, 512-feature slice) unit, tokens in index
-// order.  Polling form (READY): one wave per token, visited in the order its
-// rows become ready -- token t at its last layout row max_k pos[t,k], walking
-// the layout rows in order, which is the order the signalled down GEMM
-// completes its row tiles -- then the tokens with no row on this GPU; the
-// wave polls once for the token and then combines all of its slices.
-template <int YDT, int ODT, bool READY>
+// order.
+template <int YDT, int ODT>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ pos,
-                                                 const int32_t* __restrict__ row_src, int m_cap,
                                                  const float* __restrict__ w, int T, int K, int H,
-                                                 const void* __restrict__ shared_out, void* __restrict__ out,
-                                                 const int32_t* signals, int rows_per_sig, int threshold,
-                                                 uint64_t timeout_ticks, int32_t* status) {
+                                                 const void* __restrict__ shared_out, void* __restrict__ out) {
     __shared__ int pos_lds[4][32];
     __shared__ float w_lds[4][32];
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int n_slices = (H / 8 + kWave - 1) / kWave;
     const int64_t stride = (int64_t)gridDim.x * 4;
-    if (!READY) {
-        const int64_t n_units = (int64_t)T * n_slices;
-        for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += stride) {
-            const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
-            int none = -1;
-            token_slots(pos, w, t, K, nullptr, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv],
-                        w_lds[wv], lane, none);
-            combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
-        }
-        return;
+    const int64_t n_units = (int64_t)T * n_slices;
+    for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += stride) {
+        const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
+        token_slots(pos, w, t, K, pos_lds[wv], w_lds[wv], lane);
+        combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
     }
-    // units of RC consecutive layout rows (then of RC tokens without a row
-    // here): the tokens completed by neighbouring rows mostly share a row
-    // tile, so one confirmed poll serves them all
-    constexpr int RC = 16;
-    const int64_t row_units = ((int64_t)m_cap + RC - 1) / RC;
-    const int64_t n_units = row_units + ((int64_t)T + RC - 1) / RC;
+}
+
+// Eight features of a published row (device-scope loads: see load8_published),
+// as the raw 16 bytes of bf16 (or two 16-byte halves of fp32).
+template <int YDT>
+struct Raw;
+template <>
+struct Raw<RDG_BF16> {
+    uint64_t a, b;
+    __device__ void load(const void* y, size_t row, int H, int v) {
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const uint16_t*>(y) + row * H) + 2 * v;
+        a = __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        b = __hip_atomic_load(p + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ void fma_into(float* acc, float wk) const {
+        const uint32_t q[4] = {(uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32)};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wk * bf16_to_f32(q[i] & 0xffffu);
+            acc[2 * i + 1] += wk * bf16_to_f32(q[i] >> 16);
+        }
+    }
+};
+template <>
+struct Raw<RDG_F32> {
+    uint64_t q[4];
+    __device__ void load(const void* y, size_t row, int H, int v) {
+        const uint64_t* p = reinterpret_cast<const uint64_t*>(static_cast<const float*>(y) + row * H) + 4 * v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[i] = __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __device__ void fma_into(float* acc, float wk) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            acc[2 * i] += wk * __uint_as_float((uint32_t)q[i]);
+            acc[2 * i + 1] += wk * __uint_as_float((uint32_t)(q[i] >> 32));
+        }
+    }
+};
+
+// Device-scope direct load of 16 bytes per lane into LDS (lds + 16 * lane,
+// lds wave-uniform): the rows a concurrently running producer on another XCD
+// has published are read past this CU's L1 and any stale line of this XCD's
+// L2 (device scope), streamed (nt), and land in LDS without occupying
+// registers, so a wave can have many of them in flight.  Issued from inline
+// assembly; the caller waits for them (vmcnt) before reading the LDS.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16_device_scope(const void* src, const void* lds) {
+    typedef __attribute__((address_space(3))) void* lds_ptr_t;
+    const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off sc1 nt" ::"v"(src), "s"(l) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Polling form.  Units: one layout row each (a token is combined at its
+// last layout row, max_k pos[t,k]), then units of 64 tokens (the tokens with
+// no row here, which get the shared output or zero).  Wave g of the grid
+// takes units g, g + waves, g + 2 waves, ...: every wave's units are spread
+// over the layout, so when the down GEMM's last row tiles complete, their
+// tokens are combined by many waves at once.  Per token: lane k < K holds
+// slot k; lane 0 waits for the counter of each row tile the token reads (the
+// last confirmed tile is remembered).  Then the token's rows are staged in
+// groups: for bf16 rows, SB 512-feature pieces per wave go through LDS by
+// device-scope direct loads, all in flight at once (SB / local rows slices
+// of every local row per group), and each slice is summed in slot order in
+// fp32 -- the same sum, in the same order, as the plain form.
+template <int YDT, int ODT>
+__global__ __launch_bounds__(256) void k_combine_poll(const void* __restrict__ y, const int32_t* __restrict__ pos,
+                                                      const int32_t* __restrict__ row_src, int m_cap,
+                                                      const float* __restrict__ w, int T, int K, int H,
+                                                      const void* __restrict__ shared_out, void* __restrict__ out,
+                                                      const int32_t* signals, int rows_per_sig, int threshold,
+                                                      uint64_t timeout_ticks, int32_t* status) {
+    constexpr int SB = 8;  // staged pieces of 64 lanes x 16 bytes per wave
+    __shared__ __attribute__((aligned(16))) uint8_t stage[4][SB][1024];
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
+    const int64_t row_units = m_cap;
+    const int64_t n_units = row_units + ((int64_t)T + kWave - 1) / kWave;
+    const int nvec = H / 8, n_slices = (nvec + kWave - 1) / kWave;
     int known_tile = -1;
-    for (int64_t u = (int64_t)blockIdx.x * 4 + wv; u < n_units; u += stride) {
-        // lane i < RC looks at row u*RC+i (or token (u-row_units)*RC+i): its
-        // token, and whether this unit is where that token gets combined
+    for (int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + wv; u < n_units; u += waves) {
         int tok = -1;
         bool mine = false;
-        if (lane < RC) {
-            if (u < row_units) {
-                const int64_t r = u * RC + lane;
-                const int src = r < m_cap ? row_src[r] : -1;
+        if (u < row_units) {
+            if (lane == 0) {
+                const int src = row_src[u];
                 if (src >= 0) {
                     tok = src / K;
                     int last = -1;
                     for (int k = 0; k < K; ++k) last = max(last, pos[(size_t)tok * K + k]);
-                    mine = last == (int)r;  // the token is combined at its last row
+                    mine = last == (int)u;
                 }
-            } else {
-                const int64_t tt = (u - row_units) * RC + lane;
-                if (tt < T) {
-                    tok = (int)tt;
-                    int last = -1;
-                    for (int k = 0; k < K; ++k) last = max(last, pos[(size_t)tok * K + k]);
-                    mine = last < 0;  // no row here: combined in this second pass
-                }
+            }
+        } else {
+            const int64_t tt = (u - row_units) * kWave + lane;
+            if (tt < T) {
+                tok = (int)tt;
+                int last = -1;
+                for (int k = 0; k < K; ++k) last = max(last, pos[(size_t)tok * K + k]);
+                mine = last < 0;
             }
         }
         uint64_t todo = __ballot(mine);
@@ -296,9 +254,109 @@ __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, con
             const int i = __builtin_ctzll(todo);
             todo &= todo - 1;
             const int t = __shfl(tok, i);
-            token_slots(pos, w, t, K, signals, rows_per_sig, threshold, timeout_ticks, status, pos_lds[wv],
-                        w_lds[wv], lane, known_tile);
-            combine_token_published<YDT, ODT>(y, shared_out, out, t, K, H, pos_lds[wv], w_lds[wv], lane);
+            int p = -1;
+            float wt = 0.0f;
+            if (lane < K) {
+                p = pos[(size_t)t * K + lane];
+                wt = w[(size_t)t * K + lane];
+            }
+            for (int k = 0; k < K; ++k) {
+                const int pk = __shfl(p, k);
+                if (pk < 0) continue;
+                const int tile = pk / rows_per_sig;
+                if (tile == known_tile) continue;
+                int ok = 1;
+                if (lane == 0) {
+                    ok = wait_counter(signals + tile, threshold, timeout_ticks) ? 1 : 0;
+                    if (!ok) set_status(status, RDG_ETIMEOUT, tile);
+                }
+                ok = __shfl(ok, 0);
+                if (ok) known_tile = tile;
+                else if (lane == k) p = -1;  // skip the incomplete row
+            }
+            // the rows are read with device-scope loads; this fence keeps
+            // those loads after the polls
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+            const uint64_t slots = __ballot(lane < K && p >= 0);
+            const int nk = __popcll(slots);
+            if constexpr (YDT == RDG_BF16) {
+                // G slices of every local row per staging round (rows in
+                // rounds of SB when there are more local rows than pieces)
+                const int G = nk == 0 ? n_slices : nk >= SB ? 1 : SB / nk;
+                for (int g0 = 0; g0 < n_slices; g0 += G) {
+                    const int ng = n_slices - g0 < G ? n_slices - g0 : G;
+                    if (nk <= SB) {
+                        int j = 0;
+                        for (uint64_t m = slots; m; m &= m - 1, ++j) {
+                            const uint8_t* row =
+                                static_cast<const uint8_t*>(y) + (size_t)__shfl(p, __builtin_ctzll(m)) * H * 2;
+                            for (int s2 = 0; s2 < ng; ++s2) {
+                                const int v = (g0 + s2) * kWave + lane;
+                                dma16_device_scope(row + (size_t)(v < nvec ? v : nvec - 1) * 16, stage[wv][j * G + s2]);
+                            }
+                        }
+                        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the pieces are in LDS
+                    }
+                    for (int s2 = 0; s2 < ng; ++s2) {
+                        const int v = (g0 + s2) * kWave + lane;
+                        float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                        for (int r0 = 0; r0 < nk; r0 += SB) {
+                            uint64_t m = slots;
+                            for (int q = 0; q < r0; ++q) m &= m - 1;  // skip the rows of earlier rounds
+                            if (nk > SB) {
+                                uint64_t mm = m;
+                                for (int j = 0; j < SB && mm; ++j, mm &= mm - 1) {
+                                    const uint8_t* row =
+                                        static_cast<const uint8_t*>(y) + (size_t)__shfl(p, __builtin_ctzll(mm)) * H * 2;
+                                    dma16_device_scope(row + (size_t)(v < nvec ? v : nvec - 1) * 16, stage[wv][j]);
+                                }
+                                __builtin_amdgcn_s_waitcnt(0x0f70);
+                            }
+                            for (int j = 0; j < SB && m; ++j, m &= m - 1) {
+                                const float wk = __shfl(wt, __builtin_ctzll(m));
+                                const uint4 q = *reinterpret_cast<const uint4*>(
+                                    stage[wv][nk > SB ? j : j * G + s2] + lane * 16);
+                                const uint32_t qq[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    a[2 * e] += wk * bf16_to_f32(qq[e] & 0xffffu);
+                                    a[2 * e + 1] += wk * bf16_to_f32(qq[e] >> 16);
+                                }
+                            }
+                            if (nk > SB) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0) before restaging
+                        }
+                        if (v < nvec) {
+                            if (shared_out != nullptr) {
+                                float sv[8];
+                                load8<ODT>(shared_out, (size_t)t, H, v, sv);
+#pragma unroll
+                                for (int q = 0; q < 8; ++q) a[q] += sv[q];
+                            }
+                            store8<ODT>(out, (size_t)t, H, v, a);
+                        }
+                    }
+                    // the next group's loads overwrite the pieces: this wave's LDS reads first
+                    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+                }
+            } else {
+#pragma unroll 1
+                for (int v = lane; v < nvec; v += kWave) {
+                    float a[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                    for (uint64_t m = slots; m; m &= m - 1) {
+                        const int k = __builtin_ctzll(m);
+                        Raw<YDT> r;
+                        r.load(y, (size_t)__shfl(p, k), H, v);
+                        r.fma_into(a, __shfl(wt, k));
+                    }
+                    if (shared_out != nullptr) {
+                        float sv[8];
+                        load8<ODT>(shared_out, (size_t)t, H, v, sv);
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) a[q] += sv[q];
+                    }
+                    store8<ODT>(out, (size_t)t, H, v, a);
+                }
+            }
         }
     }
 }
@@ -311,31 +369,37 @@ hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int
                           int max_blocks, int32_t* status, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const bool ready = signals != nullptr;
-    const int64_t units = ready ? ((int64_t)m_cap + 15) / 16 + ((int64_t)T + 15) / 16
-                                : (int64_t)T * ((H / 8 + kWave - 1) / kWave);
-    int64_t blocks = (units + 3) / 4;
-    if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
+    int64_t blocks;
     if (ready) {
-        // Polling workgroups hold their CU resources while they wait.  A
-        // producer workgroup of the down GEMM needs most of a CU, so polling
-        // workgroups spread over every CU could leave it nowhere to run until
-        // the waits time out: at most a quarter of the CUs' worth of them.
+        // Polling workgroups hold their CU's resources while they wait, and a
+        // down-GEMM workgroup needs most of a CU: at most a quarter of the
+        // CUs' worth of them (fewer if max_blocks says so), so that the GEMM
+        // always keeps three quarters of the CUs.  (Beside a GEMM workgroup
+        // that leaves room for one, a polling workgroup would take no CU;
+        // but registers and LDS are allocated in contiguous ranges, and a
+        // polling workgroup placed off the gap blocks the CU for the GEMM
+        // until it exits -- not a placement the launch can control.)
         int dev = 0, n_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return hipErrorInvalidDevice;
-        const int64_t cap = n_cu / 4 > 0 ? n_cu / 4 : 1;
-        if (blocks > cap) blocks = cap;
+        const int cap = n_cu / 4 > 0 ? n_cu / 4 : 1;
+        blocks = max_blocks > 0 && max_blocks < cap ? max_blocks : cap;
+        const int64_t units = (int64_t)m_cap + ((int64_t)T + kWave - 1) / kWave;
+        if (blocks > (units + 3) / 4) blocks = (units + 3) / 4;
+    } else {
+        const int64_t units = (int64_t)T * ((H / 8 + kWave - 1) / kWave);
+        blocks = (units + 3) / 4;
+        if (max_blocks > 0 && blocks > max_blocks) blocks = max_blocks;
     }
-#define RDG_COMBINE(YD, OD)                                                                                    \
-    do {                                                                                                       \
-        if (ready)                                                                                             \
-            k_combine<YD, OD, true><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,        \
-                                                                   shared_out, out, signals, rows_per_sig,    \
-                                                                   threshold, timeout_ticks, status);         \
-        else                                                                                                   \
-            k_combine<YD, OD, false><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,       \
-                                                                    shared_out, out, nullptr, rows_per_sig,   \
-                                                                    threshold, timeout_ticks, status);        \
+#define RDG_COMBINE(YD, OD)                                                                                      \
+    do {                                                                                                         \
+        if (ready)                                                                                               \
+            k_combine_poll<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,           \
+                                                                  shared_out, out, signals, rows_per_sig,       \
+                                                                  threshold, timeout_ticks, status);            \
+        else                                                                                                     \
+            k_combine<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out);             \
     } while (0)
     if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_COMBINE(RDG_BF16, RDG_BF16);
     else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_COMBINE(RDG_BF16, RDG_F32);

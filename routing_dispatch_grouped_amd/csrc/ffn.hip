@@ -310,13 +310,14 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
             for (int rt = 0; rt < 2; ++rt) {
                 const size_t idx = (size_t)row * a.Nout + fl + rt * 16;
                 if (OUT_KIND == 0) {
-                    float4 o = make_float4(val[rt][ct][0], val[rt][ct][1], val[rt][ct][2], val[rt][ct][3]);
-                    *reinterpret_cast<float4*>(a.O + idx * 4) = o;
+                    store_out16<SIGNAL>(a.O + idx * 4,
+                                        make_float4(val[rt][ct][0], val[rt][ct][1], val[rt][ct][2], val[rt][ct][3]));
                 } else {
-                    uint2 o;
-                    o.x = f32_to_bf16(val[rt][ct][0]) | (f32_to_bf16(val[rt][ct][1]) << 16);
-                    o.y = f32_to_bf16(val[rt][ct][2]) | (f32_to_bf16(val[rt][ct][3]) << 16);
-                    *reinterpret_cast<uint2*>(a.O + idx * 2) = o;
+                    store_out8<SIGNAL>(a.O + idx * 2,
+                                       (uint64_t)(f32_to_bf16(val[rt][ct][0]) | (f32_to_bf16(val[rt][ct][1]) << 16)) |
+                                           ((uint64_t)(f32_to_bf16(val[rt][ct][2]) |
+                                                       (f32_to_bf16(val[rt][ct][3]) << 16))
+                                            << 32));
                 }
             }
         }
@@ -502,12 +503,11 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
             if (row < row_end) {
                 const size_t idx = (size_t)row * a.Nout + f0 + fl + rt * 16;
                 if (OUT_KIND == 0) {
-                    *reinterpret_cast<float4*>(a.O + idx * 4) = make_float4(v[0], v[1], v[2], v[3]);
+                    store_out16<SIGNAL>(a.O + idx * 4, make_float4(v[0], v[1], v[2], v[3]));
                 } else {
-                    uint2 o;
-                    o.x = f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16);
-                    o.y = f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16);
-                    *reinterpret_cast<uint2*>(a.O + idx * 2) = o;
+                    store_out8<SIGNAL>(a.O + idx * 2, (uint64_t)(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16)) |
+                                                          ((uint64_t)(f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16))
+                                                           << 32));
                 }
             }
         }

@@ -594,10 +594,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
             const int row = row0 + c;
 #pragma unroll
             for (int ot = 0; ot < NOT; ++ot) {
-                uint2 o;
-                o.x = f32_to_bf16(acc[ot][ct][0]) | (f32_to_bf16(acc[ot][ct][1]) << 16);
-                o.y = f32_to_bf16(acc[ot][ct][2]) | (f32_to_bf16(acc[ot][ct][3]) << 16);
-                *reinterpret_cast<uint2*>(a.O + ((size_t)row * a.Nout + fl + ot * 16) * 2) = o;
+                const uint64_t o = (uint64_t)(f32_to_bf16(acc[ot][ct][0]) | (f32_to_bf16(acc[ot][ct][1]) << 16)) |
+                                   ((uint64_t)(f32_to_bf16(acc[ot][ct][2]) | (f32_to_bf16(acc[ot][ct][3]) << 16))
+                                    << 32);
+                store_out8<SIGNAL>(a.O + ((size_t)row * a.Nout + fl + ot * 16) * 2, o);
             }
         }
     }
@@ -645,19 +645,22 @@ bool tiled_supported(int dtype, int H, int I) {
     return false;
 }
 
+// power-of-two scales: 64 weight rows per wave when the row tiles times the
+// wider gate/up panels fill the CUs several times over, else 32.  n_tiles_max
+// bounds the tiles from the dispatched slots, which can be several times the
+// rows that arrive (a rank's share), hence the margin.
+static bool pow2_wide(const FfnCall& c) {
+    return shapes_ok<RDG_FP8_E4M3, true>(c.H, c.I) &&
+           (int64_t)c.n_tiles_max * (c.I / (panel_rows<RDG_FP8_E4M3, true>() / 2)) >= 4 * 256;
+}
+
 hipError_t launch_ffn_tiled(const FfnCall& c, hipStream_t s) {
     if (c.n_tiles_max <= 0) return hipSuccess;
     if (!tiled_supported(c.dtype, c.H, c.I)) return hipErrorInvalidValue;
     if (c.dtype == RDG_BF16) return launch_dt<RDG_BF16, false, true>(c, s);
     if (c.dtype != RDG_FP8_E4M3) return hipErrorInvalidValue;
     if (!c.pow2) return launch_dt<RDG_FP8_E4M3, false, false>(c, s);
-    // power-of-two scales: 64 weight rows per wave when the row tiles times
-    // the wider gate/up panels fill the CUs several times over, else 32.
-    // n_tiles_max bounds the tiles from the dispatched slots, which can be
-    // several times the rows that arrive (a rank's share), hence the margin.
-    const bool wide = shapes_ok<RDG_FP8_E4M3, true>(c.H, c.I) &&
-                      (int64_t)c.n_tiles_max * (c.I / (panel_rows<RDG_FP8_E4M3, true>() / 2)) >= 4 * 256;
-    return wide ? launch_dt<RDG_FP8_E4M3, true, true>(c, s) : launch_dt<RDG_FP8_E4M3, true, false>(c, s);
+    return pow2_wide(c) ? launch_dt<RDG_FP8_E4M3, true, true>(c, s) : launch_dt<RDG_FP8_E4M3, true, false>(c, s);
 }
 
 }  // namespace rdg

@@ -142,20 +142,39 @@ hipError_t launch_layout_dense(int T, const rdg_layout& L, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
 hipError_t launch_pack(const void* W, int dtype, int n_mat, int rows, int cols, void* P, hipStream_t s);
 
+// Output stores of a signalled down GEMM: device scope, so they are written
+// through to memory instead of staying dirty in this XCD's L2, where another
+// XCD's consumer could not see them.  (Plain stores with a device-scope
+// release before the signal would need a write-back of the whole L2 per
+// workgroup: the down GEMM ran 20% slower that way.)
+template <bool SIGNAL>
+__device__ __forceinline__ void store_out8(void* p, uint64_t v) {
+    if constexpr (SIGNAL) __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *static_cast<uint64_t*>(p) = v;
+}
+template <bool SIGNAL>
+__device__ __forceinline__ void store_out16(void* p, float4 v) {
+    if constexpr (SIGNAL) {
+        store_out8<true>(p, (uint64_t)__float_as_uint(v.x) | ((uint64_t)__float_as_uint(v.y) << 32));
+        store_out8<true>(static_cast<uint8_t*>(p) + 8,
+                         (uint64_t)__float_as_uint(v.z) | ((uint64_t)__float_as_uint(v.w) << 32));
+    } else {
+        *static_cast<float4*>(p) = v;
+    }
+}
+
 // End of a signalled down-GEMM workgroup: publish `cols` finished output
-// columns of its row tile.  Every wave first waits for its own stores (they
-// are then in this XCD's L2); after the barrier one wave releases at device
-// scope -- on this part a write-back of the XCD's L2 to memory, where other
-// XCDs' device-scope loads read -- and adds to the counter.  Deliberately no
-// __threadfence(): its acquire half also invalidates the XCD's L2, throwing
-// away the weight panels the other workgroups on that XCD are re-reading.
+// columns of its row tile.  Every wave waits for its own output stores to
+// complete -- device-scope stores, so they are then in memory, where other
+// XCDs' device-scope loads read -- the waves meet at a barrier, and one
+// thread adds the column count to the tile's counter (relaxed, device
+// scope).  No fence: a device-scope release would also write back this XCD's
+// whole L2, and its acquire half would invalidate it, throwing away the
+// weight panels the other workgroups on this XCD are re-reading.
 __device__ __forceinline__ void signal_done(int32_t* counter, int cols) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (threadIdx.x == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(counter, cols, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(counter, cols, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Column blocks of a signalled (tile-major) down GEMM grid, padded to a

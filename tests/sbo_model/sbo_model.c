@@ -10,15 +10,24 @@
  * each executed by a team of threads: every thread stores its share of the
  * tile's panel (plain stores), the team meets at a barrier, then one thread
  * publishes: a release add of the panel's column count to the tile's counter
- * (the GPU code issues a release fence and a relaxed add; ThreadSanitizer
- * does not model standalone fences, and the release add is the equivalent
- * form -- the adds of all panels form one release sequence).  Consumer:
+ * (the adds of all panels form one release sequence; the GPU code instead
+ * stores the rows at device scope, waits for them to complete and adds with
+ * no fence -- see below).  Consumer:
  * threads walk the layout rows in chunks and combine each token at its last
  * row: poll every counter the token reads (relaxed loads) until it reaches H,
  * then an acquire load of it, then plain reads of the rows; tokens with no
- * row are combined in a second pass.  The GPU consumer reads the rows with
- * device-scope loads instead of acquiring (that avoids an L2 invalidation);
- * the acquire is their C11 counterpart.
+ * row are combined in a second pass.
+ *
+ * What this model does not cover: C11 has no memory scopes, and
+ * ThreadSanitizer does not follow standalone fences, so the acquire load
+ * stands for "relaxed poll, then acquire", and the release add for "stores,
+ * then release".  The GPU producer stores its rows at device scope and waits
+ * for them to complete before a relaxed add; the GPU consumer issues a
+ * workgroup-scope fence after its polls and reads the rows with device-scope
+ * loads.  Neither side writes back or invalidates an XCD's L2 (the down
+ * GEMM's weight panels live there).  That is not a C11 pattern; it relies on
+ * the GPU's cache rules, which test_sbo_hw_model.py states and checks
+ * exhaustively on an operational model of per-XCD write-back L2 caches.
  *
  * Build with -DBROKEN to drop the consumer's wait: ThreadSanitizer must then
  * report a race (the test checks that the model can fail).
