@@ -59,6 +59,9 @@ def parse():
     p.add_argument("--summary", choices=["auto", "on", "off"], default="auto",
                    help="also measure every other workload and report it under 'workloads' (auto: with the "
                         "default workload and no variant flags)")
+    p.add_argument("--extras", choices=["on", "off"], default="on",
+                   help="the measurements after the timed steps: heavy_experts (prefill layers) and the sbo "
+                        "comparison (prefill rank share); off for a kernel trace of the timed steps alone")
     p.add_argument("--graph", action="store_true",
                    help="time replays of the step captured in a HIP graph (full-layer workloads); the gate/up "
                         "kernel's own time then comes from as many eager steps run after them")
@@ -67,6 +70,9 @@ def parse():
     p.add_argument("--eplb-replicas", choices=["greedy", "one_each"], default=None,
                    help="rank shares: the EPLB plan's replica rule (default greedy: each of the 32 redundant "
                         "copies to the expert with the largest expected load per copy)")
+    p.add_argument("--side-cus", type=int, default=0,
+                   help="full layers: the shared expert's stream may use only this many CUs, spread evenly over "
+                        "the GPU (a CU-masked stream); 0: all CUs")
     p.add_argument("--tbo", action="store_true",
                    help="prefill layers as two micro-batches cut at a sequence boundary, on two streams "
                         "(the roofline then covers micro-batch A's gate/up)")
@@ -114,6 +120,35 @@ def measured_traffic(workload):
         return None
 
 
+def cu_masked_stream(n_cus):
+    """A stream whose kernels may run only on n_cus of the GPU's CUs, spread
+    evenly (hipExtStreamCreateWithCUMask, default priority), as a torch
+    external stream."""
+    import ctypes
+
+    import torch
+    # the HIP runtime already loaded in this process (torch's), not a second copy
+    path = "libamdhip64.so"
+    for line in open("/proc/self/maps"):
+        if "libamdhip64" in line:
+            path = line.split()[-1]
+            break
+    hip = ctypes.CDLL(path)
+    hip.hipExtStreamCreateWithCUMask.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint32,
+                                                 ctypes.POINTER(ctypes.c_uint32)]
+    total = torch.cuda.get_device_properties(0).multi_processor_count
+    n_cus = max(1, min(n_cus, total))
+    words = (ctypes.c_uint32 * ((total + 31) // 32))()
+    for j in range(n_cus):
+        cu = j * total // n_cus
+        words[cu // 32] |= 1 << (cu % 32)
+    stream = ctypes.c_void_p()
+    rc = hip.hipExtStreamCreateWithCUMask(ctypes.byref(stream), len(words), words)
+    if rc != 0:
+        raise RuntimeError("hipExtStreamCreateWithCUMask failed (%d)" % rc)
+    return torch.cuda.ExternalStream(stream.value)
+
+
 def layer_bytes(cfg, T, R, A, esz):
     """Algorithmic HBM bytes of one whole step (every kernel's reads and
     writes counted once: no padding, no unused masked capacity): routing (or,
@@ -141,7 +176,7 @@ def layer_bytes(cfg, T, R, A, esz):
 class Bench:
     """Buffers and the step of one workload."""
 
-    def __init__(self, name, dev, ue8m0=False, tbo=False, replicas=None):
+    def __init__(self, name, dev, ue8m0=False, tbo=False, replicas=None, side_cus=0, side_stream=None):
         import torch
 
         import routing_dispatch_grouped_amd as rdg
@@ -170,10 +205,13 @@ class Bench:
         self.stream = torch.cuda.current_stream()
         self.rank = "B_global" in cfg
         self.tbo = None
+        self.side_cus = side_cus
         if self.rank:
             self._setup_rank()
         else:
             self._setup_full()
+            if side_cus:
+                self.side = side_stream if side_stream is not None else cu_masked_stream(side_cus)
             if tbo:
                 self._setup_tbo()
         self._setup_rotation()
@@ -569,6 +607,8 @@ def measure(b, args, steps, warmup, workload):
             "weight_sets": len(b.weight_sets)}
     if b.tbo:
         conf["tbo_micro_batches"] = [mb["T"] for mb in b.tbo]
+    if b.side_cus:
+        conf["shared_expert_cus"] = b.side_cus
     if b.fp8:
         conf["fp8_scales"] = "ue8m0 (power of two)" if b.ue8m0 else "fp32"
     if "m_max" in cfg:
@@ -660,16 +700,19 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
-    b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo, replicas=args.eplb_replicas)
+    # a CU-masked stream needs a hardware queue of its own: created first
+    side = cu_masked_stream(args.side_cus) if args.side_cus else None
+    b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo, replicas=args.eplb_replicas, side_cus=args.side_cus,
+              side_stream=side)
     res = measure(b, args, args.steps, args.warmup, args.workload)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": res["dtype"], "data": "synthetic", "config": res["config"],
             "roofline": res["roofline"], "layer": res["layer"]}
-    if b.rank and b.signals is not None:
+    if b.rank and b.signals is not None and args.extras == "on":
         line["sbo"] = sbo_compare(b, args.steps)
         line["sbo"]["polling_workgroups"] = b.poll_blocks
-    if not b.rank and b.cfg["layout"] == "contiguous" and b.cfg["H"] >= 1024 and not args.tbo:
+    if not b.rank and b.cfg["layout"] == "contiguous" and b.cfg["H"] >= 1024 and not args.tbo and args.extras == "on":
         line["heavy_experts"] = heavy_experts(b)
     n_cpu = CPU_TOKENS[args.workload] if args.cpu_tokens is None else args.cpu_tokens
     if n_cpu != 0:
@@ -682,7 +725,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     summary = args.summary == "on" or (args.summary == "auto" and args.workload == DEFAULT_WORKLOAD and
-                                       not (args.graph or args.tbo or args.ue8m0 or args.eplb_replicas))
+                                       not (args.graph or args.tbo or args.ue8m0 or args.eplb_replicas or
+                                            args.side_cus))
     del b
     torch.cuda.empty_cache()
     if summary:
