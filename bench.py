@@ -62,6 +62,9 @@ def parse():
     p.add_argument("--extras", choices=["on", "off"], default="on",
                    help="the measurements after the timed steps: heavy_experts (prefill layers) and the sbo "
                         "comparison (prefill rank share); off for a kernel trace of the timed steps alone")
+    p.add_argument("--payload", choices=["gather", "copy"], default="gather",
+                   help="dispatch payload: gather (the dispatch builds the layout only and the gate/up GEMM reads "
+                        "each row's token through row_src) or copy (rows permuted into x_perm by the dispatch)")
     p.add_argument("--graph", action="store_true",
                    help="time replays of the step captured in a HIP graph (full-layer workloads); the gate/up "
                         "kernel's own time then comes from as many eager steps run after them")
@@ -149,12 +152,14 @@ def cu_masked_stream(n_cus):
     return torch.cuda.ExternalStream(stream.value)
 
 
-def layer_bytes(cfg, T, R, A, esz):
+def layer_bytes(cfg, T, R, A, esz, gather=False):
     """Algorithmic HBM bytes of one whole step (every kernel's reads and
     writes counted once: no padding, no unused masked capacity): routing (or,
     for a rank's share, the replica remap), the stable ranks and the row
     permutation, the routed gate/up and down GEMMs, the shared expert where
-    there is one, and the combine.  fp8 block scales are 4-byte floats."""
+    there is one, and the combine.  fp8 block scales are 4-byte floats.
+    gather: the permutation only publishes pos and row_src, and the gate/up
+    GEMM reads the R rows' tokens through them (counted with the GEMM)."""
     H, I, K, N = cfg["H"], cfg["I"], cfg["K"], cfg["N"]
     ysz = 4 if cfg["dtype"] == "f32" else 2
     sc = 4 if cfg["dtype"] == "fp8" else 0
@@ -163,7 +168,10 @@ def layer_bytes(cfg, T, R, A, esz):
     Tsh = cfg.get("own_tokens", T) if rank else T
     b = T * K * 8 + T * 8 if rank else T * N * 4 + T * K * 8            # remap / route
     b += T * K * 8                                                       # stable ranks
-    b += T * H * esz + R * H * esz + (T + R) * (H // 128) * sc           # permute rows
+    if gather:
+        b += T * K * 4 + R * 4                                           # publish pos, row_src
+    else:
+        b += T * H * esz + R * H * esz + (T + R) * (H // 128) * sc       # permute rows
     b += A * 2 * I * H * esz + A * 2 * (I // 128) * (H // 128) * sc + R * (H + I) * esz + R * (H + I) // 128 * sc
     b += A * I * H * esz + A * (I // 128) * (H // 128) * sc + R * (I * esz + H * ysz) + R * (I // 128) * sc
     if shI:
@@ -176,7 +184,8 @@ def layer_bytes(cfg, T, R, A, esz):
 class Bench:
     """Buffers and the step of one workload."""
 
-    def __init__(self, name, dev, ue8m0=False, tbo=False, replicas=None, side_cus=0, side_stream=None):
+    def __init__(self, name, dev, ue8m0=False, tbo=False, replicas=None, side_cus=0, side_stream=None,
+                 payload="gather"):
         import torch
 
         import routing_dispatch_grouped_amd as rdg
@@ -202,6 +211,9 @@ class Bench:
         self.ydt = torch.float32 if cfg["dtype"] == "f32" else torch.bfloat16
         self.YDT = rdg.RDG_F32 if cfg["dtype"] == "f32" else rdg.RDG_BF16
         self.events = []
+        # gather: the dispatch builds the layout only and the gate/up GEMM
+        # reads the tokens through row_src; copy: rows permuted into x_perm
+        self.gather = payload == "gather"
         self.stream = torch.cuda.current_stream()
         self.rank = "B_global" in cfg
         self.tbo = None
@@ -277,11 +289,13 @@ class Bench:
         H, I = cfg["H"], cfg["I"]
         self.L = rdg.Layout(kind, n_local, T, K, self.dev, block_m=block_m, m_max=m_max)
         m_cap = self.L.m_cap
-        self.x_perm = torch.empty((m_cap, H), dtype=self.sdt, device=self.dev)
         self.h = torch.empty((m_cap, I), dtype=self.sdt, device=self.dev)
         self.y = torch.empty((m_cap, H), dtype=self.ydt, device=self.dev)
         fp8 = self.fp8
-        self.x_perm_s = torch.empty((m_cap, H // 128), dtype=torch.float32, device=self.dev) if fp8 else None
+        self.x_perm = self.x_perm_s = None
+        if not self.gather:
+            self.x_perm = torch.empty((m_cap, H), dtype=self.sdt, device=self.dev)
+            self.x_perm_s = torch.empty((m_cap, H // 128), dtype=torch.float32, device=self.dev) if fp8 else None
         self.h_s = torch.empty((m_cap, I // 128), dtype=torch.float32, device=self.dev) if fp8 else None
 
     def _shared_buffers(self, T):
@@ -300,6 +314,7 @@ class Bench:
         self.logits_np = synth.logits(cfg)
         self.logits = torch.from_numpy(self.logits_np).to(self.dev)
         self.x = synth.x(cfg, B, device=self.dev)
+        self.x_s = None
         self.W, self.S = self._experts(range(N))
         self.Wsh, self.Ssh = self._experts([0], shared=True)
         self.ids = torch.empty((B, K), dtype=torch.int32, device=self.dev)
@@ -326,7 +341,7 @@ class Bench:
             L = rdg.Layout(rdg.RDG_CONTIGUOUS, N, T, K, self.dev, block_m=128)
             mb = dict(t0=t0, T=T, L=L, x=self.x[t0:t1], logits=self.logits[t0:t1], ids=self.ids[t0:t1],
                       tw=self.tw[t0:t1], out=self.out[t0:t1], ys=self.ys[t0:t1],
-                      x_perm=torch.empty((L.m_cap, H), dtype=self.sdt, device=self.dev),
+                      x_perm=(None if self.gather else torch.empty((L.m_cap, H), dtype=self.sdt, device=self.dev)),
                       h=torch.empty((L.m_cap, I), dtype=self.sdt, device=self.dev),
                       y=torch.empty((L.m_cap, H), dtype=self.ydt, device=self.dev))
             self.tbo.append(mb)
@@ -357,8 +372,12 @@ class Bench:
                     e0 = torch.cuda.Event(enable_timing=True)
                     e1 = torch.cuda.Event(enable_timing=True)
                     e0.record(st)
-                rdg.rdg_grouped_gate_up(mb["L"], self.DT, H, I, mb["x_perm"], None, self.W["W1"], self.W["W3"], None,
-                                        None, mb["h"], None, stream=st)
+                if self.gather:
+                    rdg.rdg_grouped_gate_up_gather(mb["L"], self.DT, H, I, mb["x"], None, K, self.W["W1"],
+                                                   self.W["W3"], None, None, mb["h"], None, stream=st)
+                else:
+                    rdg.rdg_grouped_gate_up(mb["L"], self.DT, H, I, mb["x_perm"], None, self.W["W1"], self.W["W3"],
+                                            None, None, mb["h"], None, stream=st)
                 if timed and mb is A:
                     e1.record(st)
                     self.events.append((e0, e1))
@@ -436,8 +455,13 @@ class Bench:
             e0 = self.torch.cuda.Event(enable_timing=True)
             e1 = self.torch.cuda.Event(enable_timing=True)
             e0.record(self.torch.cuda.current_stream())
-        rdg.rdg_grouped_gate_up(self.L, self.DT, cfg["H"], cfg["I"], self.x_perm, self.x_perm_s, self.W["W1"],
-                                self.W["W3"], self.S.get("W1"), self.S.get("W3"), self.h, self.h_s)
+        if self.gather:
+            rdg.rdg_grouped_gate_up_gather(self.L, self.DT, cfg["H"], cfg["I"], self.x, self.x_s, cfg["K"],
+                                           self.W["W1"], self.W["W3"], self.S.get("W1"), self.S.get("W3"), self.h,
+                                           self.h_s)
+        else:
+            rdg.rdg_grouped_gate_up(self.L, self.DT, cfg["H"], cfg["I"], self.x_perm, self.x_perm_s, self.W["W1"],
+                                    self.W["W3"], self.S.get("W1"), self.S.get("W3"), self.h, self.h_s)
         if timed:
             e1.record(self.torch.cuda.current_stream())
             self.events.append((e0, e1))
@@ -469,7 +493,7 @@ class Bench:
             else:
                 self._shared(self.x, None, self.T)
             rdg.rdg_route(self.logits, cfg["n_group"], cfg["topk_group"], K, cfg["scale"], self.ids, self.tw)
-            rdg.rdg_dispatch(self.x, None, self.DT, self.ids, self.L, self.x_perm)
+            rdg.rdg_dispatch(self.x, None, self.DT, self.ids, self.L, self.x_perm)  # gather: x_perm None
             self._gate_up(timed)
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
             if self.overlap_shared:
@@ -478,7 +502,8 @@ class Bench:
             return
         plan = self.plan
         rdg.rdg_eplb_remap(self.ids, self.gidx, self.l2p, self.nrep, plan["phys_begin"], plan["n_local"], self.local)
-        rdg.rdg_dispatch(self.x, self.x_s, self.DT, self.local, self.L, self.x_perm, self.x_perm_s)
+        rdg.rdg_dispatch(self.x, self.x_s if not self.gather else None, self.DT, self.local, self.L, self.x_perm,
+                         self.x_perm_s)
         if self.signals is None:
             self._gate_up(timed)
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
@@ -545,7 +570,7 @@ def _stats(b):
 
 def _roofline(cfg, active, rows, gate_ms, workload):
     """Roofline of one gate/up launch: algorithmic bytes (W1 and W3 of every
-    active expert, + fp8 block scales; the routed rows of x_perm read once, h
+    active expert, + fp8 block scales; the routed rows' tokens read once, h
     written once) and flops 4 R H I; the bound is whichever of bytes / 8 TB/s
     and flops / MFMA peak is the longer."""
     H, I = cfg["H"], cfg["I"]
@@ -604,7 +629,8 @@ def measure(b, args, steps, warmup, workload):
             "n_group": cfg["n_group"], "topk_group": cfg["topk_group"], "shared_I": cfg["shared_I"],
             "layout": cfg["layout"], "active_experts": active, "routed_rows": rows,
             "load_balance_mean_over_max": round(balance, 4), "graph": bool(args.graph),
-            "weight_sets": len(b.weight_sets)}
+            "weight_sets": len(b.weight_sets),
+            "dispatch_payload": "gathered by the gate/up GEMM" if b.gather else "copied into x_perm"}
     if b.tbo:
         conf["tbo_micro_batches"] = [mb["T"] for mb in b.tbo]
     if b.side_cus:
@@ -618,7 +644,7 @@ def measure(b, args, steps, warmup, workload):
                     eplb_replicas=b.plan["rule"], measured_rank=b.plan["rank"],
                     rank_rows_max_over_mean=round(max(b.rank_rows) * len(b.rank_rows) / sum(b.rank_rows), 4),
                     rows_per_local_expert=b.L.masked_m.cpu().tolist())
-    lb = layer_bytes(cfg, b.T, rows, active, esz)
+    lb = layer_bytes(cfg, b.T, rows, active, esz, gather=b.gather)
     layer = {"algorithmic_bytes": lb, "achieved": lb / (ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
              "frac": lb / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS}
     return {"metric": metric, "value": value, "unit": unit, "ms_per_step": ms, "dtype": cfg["dtype"],
@@ -703,7 +729,7 @@ def main():
     # a CU-masked stream needs a hardware queue of its own: created first
     side = cu_masked_stream(args.side_cus) if args.side_cus else None
     b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo, replicas=args.eplb_replicas, side_cus=args.side_cus,
-              side_stream=side)
+              side_stream=side, payload=args.payload)
     res = measure(b, args, args.steps, args.warmup, args.workload)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",
@@ -742,7 +768,7 @@ def summarise(names, args):
     out = {}
     for name in names:
         try:
-            b = Bench(name, "cuda:0")
+            b = Bench(name, "cuda:0", payload=args.payload)
             r = measure(b, args, 10, 3, name)
             entry = {"value": r["value"], "unit": r["unit"], "ms_per_step": r["ms_per_step"], "dtype": r["dtype"],
                      "roofline": {k: r["roofline"][k] for k in ("bound", "frac", "achieved", "unit", "avg_ms",

@@ -8,6 +8,8 @@
  *   rdg_tbo_split    two-batch-overlap cut of a batch into micro-batches (host)
  *   rdg_dispatch     token -> expert permutation into a contiguous or masked layout
  *   rdg_grouped_ffn  grouped gate/up GEMM + SiLU-gated product + down GEMM
+ *                    (rdg_grouped_ffn_gather: reading the token rows through
+ *                    the layout instead of a permuted copy)
  *   rdg_combine      routing-weighted unpermute-and-sum (optionally polling
  *                    the down GEMM's per-row-tile completion signals)
  *
@@ -200,6 +202,10 @@ size_t rdg_dispatch_workspace_bytes(int T, int K, int n_local);
  * layout is deterministic.  Overflow drops the extra rows and sets status
  * RDG_ECAPACITY (masked: detail = the largest count; contiguous: detail =
  * the rows needed).  Padding rows of x_perm are left untouched.
+ * x_perm = NULL (and x_perm_scales = NULL): the layout only -- counts,
+ * offsets, pos, row_src, tile tables -- and no rows are copied; x and
+ * x_scales are then not read (may be NULL).  The grouped GEMMs read the rows
+ * through row_src instead (rdg_grouped_ffn_gather).
  * H must be a multiple of 16 (fp8: of 128).  T = 0 is allowed (the layout
  * is cleared; x, ids, x_perm and the scale pointers may then be NULL). */
 int rdg_dispatch(const void* x, const float* x_scales, int dtype, int T, int H, const int32_t* ids, int K,
@@ -288,6 +294,28 @@ int rdg_grouped_gate_up(const rdg_layout* L, int dtype, int H, int I, const void
                         float* h_scales_ws, rdg_stream_t stream);
 int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h_ws, const float* h_scales_ws,
                      const void* W2, const float* W2_s, void* y, int32_t* signals, rdg_stream_t stream);
+
+/* The grouped FFN reading its token rows straight from the dispatched
+ * tokens instead of a permuted copy: the dispatch's row permutation ([H100]
+ * "DeepGEMM integration": rows ordered by expert for the contiguous grouped
+ * GEMM; [DEEP] "EP": each token's vector goes to each of its K experts)
+ * folded into the gate/up GEMM's loads.  Same arguments, rules and results
+ * as rdg_grouped_ffn / rdg_grouped_gate_up, bit for bit, except:
+ *   x         [n_rows / K, H] the tokens given to rdg_dispatch (dtype)
+ *   x_scales  [n_rows / K, H/128] fp32 (fp8 only, else NULL)
+ *   K         the slots per token of that dispatch
+ * Layout row r of expert e reads token row_src[r] / K.  L must be the
+ * layout of an rdg_dispatch (or rdg_dispatch_noalloc) of those tokens --
+ * with x_perm = NULL, which skips the copy -- whose row_src this reads;
+ * not a layout from rdg_layout_dense.  RDG_EINVAL when K is outside
+ * [1, 32], L has no row_src, or L->n_rows is not a multiple of K. */
+int rdg_grouped_ffn_gather(const rdg_layout* L, int dtype, int H, int I, const void* x, const float* x_scales, int K,
+                           const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
+                           const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,
+                           rdg_stream_t stream);
+int rdg_grouped_gate_up_gather(const rdg_layout* L, int dtype, int H, int I, const void* x, const float* x_scales,
+                               int K, const void* W1, const void* W3, const float* W1_s, const float* W3_s,
+                               void* h_ws, float* h_scales_ws, rdg_stream_t stream);
 
 /* Rows per signal counter (the grouped GEMMs' row tile for this layout,
  * type and size: 16, 32, 64 or 128) and the counter value that means "row

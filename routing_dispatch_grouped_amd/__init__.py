@@ -52,6 +52,8 @@ _SIGS = {
     "rdg_grouped_ffn": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_grouped_gate_up": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_grouped_down": ([_LP, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P], _I),
+    "rdg_grouped_ffn_gather": ([_LP, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P], _I),
+    "rdg_grouped_gate_up_gather": ([_LP, _I, _I, _I, _P, _P, _I, _P, _P, _P, _P, _P, _P, _P], _I),
     "rdg_signal_rows": ([_LP, _I, _I, _I], _I),
     "rdg_signal_threshold": ([_I, _I], _I),
     "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I64, _I, _P], _I),
@@ -215,6 +217,20 @@ def rdg_grouped_gate_up(layout, dtype, H, I, x_perm, x_perm_scales, W1, W3, W1_s
     _check(_lib.rdg_grouped_gate_up(layout.ref, dtype, H, I, _ptr(x_perm), _ptr(x_perm_scales), _ptr(W1), _ptr(W3),
                                     _ptr(W1_s), _ptr(W3_s), _ptr(h_ws), _ptr(h_scales_ws), _stream(stream)),
            "rdg_grouped_gate_up")
+
+
+def rdg_grouped_ffn_gather(layout, dtype, H, I, x, x_scales, K, W1, W3, W2, W1_s, W3_s, W2_s, h_ws, h_scales_ws,
+                           y, signals=None, stream=None):
+    _check(_lib.rdg_grouped_ffn_gather(layout.ref, dtype, H, I, _ptr(x), _ptr(x_scales), K, _ptr(W1), _ptr(W3),
+                                       _ptr(W2), _ptr(W1_s), _ptr(W3_s), _ptr(W2_s), _ptr(h_ws), _ptr(h_scales_ws),
+                                       _ptr(y), _ptr(signals), _stream(stream)), "rdg_grouped_ffn_gather")
+
+
+def rdg_grouped_gate_up_gather(layout, dtype, H, I, x, x_scales, K, W1, W3, W1_s, W3_s, h_ws, h_scales_ws,
+                               stream=None):
+    _check(_lib.rdg_grouped_gate_up_gather(layout.ref, dtype, H, I, _ptr(x), _ptr(x_scales), K, _ptr(W1), _ptr(W3),
+                                           _ptr(W1_s), _ptr(W3_s), _ptr(h_ws), _ptr(h_scales_ws), _stream(stream)),
+           "rdg_grouped_gate_up_gather")
 
 
 def rdg_grouped_down(layout, dtype, H, I, h_ws, h_scales_ws, W2, W2_s, y, signals=None, stream=None):

@@ -136,11 +136,14 @@ static int dispatch_esz(const void* x, const float* x_scales, int dtype, int T, 
         case RDG_FP8_E4M3_UE8M0:
             esz = 1;
             if (H % 128 != 0) return 0;
-            if (T > 0 && (!x_scales || !x_perm_scales)) return 0;
+            if (T > 0 && x_perm && (!x_scales || !x_perm_scales)) return 0;
             break;
         default: return 0;
     }
-    if (T > 0 && (!x || !ids || !x_perm || !aligned16(x) || !aligned16(x_perm))) return 0;
+    // x_perm NULL: the layout only (x, x_scales unused; a gathering GEMM reads the tokens)
+    if (!x_perm && x_perm_scales) return 0;
+    if (T > 0 && !ids) return 0;
+    if (T > 0 && x_perm && (!x || !aligned16(x) || !aligned16(x_perm))) return 0;
     return esz;
 }
 
@@ -183,11 +186,16 @@ int rdg_signal_threshold(int H, int dtype) {
     return H;  // each down-GEMM workgroup adds the number of output columns it stored
 }
 
+// gather_k > 0: x holds the dispatched tokens [n_rows / gather_k, H] and
+// layout row r reads token row_src[r] / gather_k (the layout must come from
+// rdg_dispatch, whose row_src it is); 0: x holds the layout rows.
 static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const void* x_perm,
-                            const float* x_perm_scales, const void* W1, const void* W3, const void* W2,
+                            const float* x_perm_scales, int gather_k, const void* W1, const void* W3, const void* W2,
                             const float* W1_s, const float* W3_s, const float* W2_s, void* h_ws, float* h_scales_ws,
                             void* y, int32_t* signals, int stages, rdg_stream_t stream) {
     if (!layout_ok(L) || H < 128 || H % 128 != 0 || I < 128 || I % 128 != 0) return RDG_EINVAL;
+    if (gather_k < 0 || gather_k > 32 || (gather_k > 0 && (!L->row_src || L->n_rows % gather_k != 0)))
+        return RDG_EINVAL;
     if (dtype != RDG_F32 && dtype != RDG_BF16 && dtype != RDG_FP8_E4M3 && dtype != RDG_FP8_E4M3_UE8M0)
         return RDG_EINVAL;
     if (L->n_rows == 0) return RDG_OK;  // nothing dispatched: no rows, nothing to launch
@@ -225,6 +233,8 @@ static int grouped_ffn_impl(const rdg_layout* L, int dtype, int H, int I, const 
     c.I = I;
     c.x = x_perm;
     c.x_s = x_perm_scales;
+    c.gather = gather_k > 0 ? L->row_src : nullptr;
+    c.gather_k = gather_k;
     c.W1 = W1;
     c.W3 = W3;
     c.W2 = W2;
@@ -244,20 +254,37 @@ int rdg_grouped_ffn(const rdg_layout* L, int dtype, int H, int I, const void* x_
                     const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
                     const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,
                     rdg_stream_t stream) {
-    return grouped_ffn_impl(L, dtype, H, I, x_perm, x_perm_scales, W1, W3, W2, W1_s, W3_s, W2_s, h_ws, h_scales_ws,
-                            y, signals, 3, stream);
+    return grouped_ffn_impl(L, dtype, H, I, x_perm, x_perm_scales, 0, W1, W3, W2, W1_s, W3_s, W2_s, h_ws,
+                            h_scales_ws, y, signals, 3, stream);
+}
+
+int rdg_grouped_ffn_gather(const rdg_layout* L, int dtype, int H, int I, const void* x, const float* x_scales, int K,
+                           const void* W1, const void* W3, const void* W2, const float* W1_s, const float* W3_s,
+                           const float* W2_s, void* h_ws, float* h_scales_ws, void* y, int32_t* signals,
+                           rdg_stream_t stream) {
+    if (K < 1) return RDG_EINVAL;
+    return grouped_ffn_impl(L, dtype, H, I, x, x_scales, K, W1, W3, W2, W1_s, W3_s, W2_s, h_ws, h_scales_ws, y,
+                            signals, 3, stream);
+}
+
+int rdg_grouped_gate_up_gather(const rdg_layout* L, int dtype, int H, int I, const void* x, const float* x_scales,
+                               int K, const void* W1, const void* W3, const float* W1_s, const float* W3_s,
+                               void* h_ws, float* h_scales_ws, rdg_stream_t stream) {
+    if (K < 1) return RDG_EINVAL;
+    return grouped_ffn_impl(L, dtype, H, I, x, x_scales, K, W1, W3, nullptr, W1_s, W3_s, nullptr, h_ws, h_scales_ws,
+                            nullptr, nullptr, 1, stream);
 }
 
 int rdg_grouped_gate_up(const rdg_layout* L, int dtype, int H, int I, const void* x_perm, const float* x_perm_scales,
                         const void* W1, const void* W3, const float* W1_s, const float* W3_s, void* h_ws,
                         float* h_scales_ws, rdg_stream_t stream) {
-    return grouped_ffn_impl(L, dtype, H, I, x_perm, x_perm_scales, W1, W3, nullptr, W1_s, W3_s, nullptr, h_ws,
+    return grouped_ffn_impl(L, dtype, H, I, x_perm, x_perm_scales, 0, W1, W3, nullptr, W1_s, W3_s, nullptr, h_ws,
                             h_scales_ws, nullptr, nullptr, 1, stream);
 }
 
 int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h_ws, const float* h_scales_ws,
                      const void* W2, const float* W2_s, void* y, int32_t* signals, rdg_stream_t stream) {
-    return grouped_ffn_impl(L, dtype, H, I, nullptr, nullptr, nullptr, nullptr, W2, nullptr, nullptr, W2_s,
+    return grouped_ffn_impl(L, dtype, H, I, nullptr, nullptr, 0, nullptr, nullptr, W2, nullptr, nullptr, W2_s,
                             const_cast<void*>(h_ws), const_cast<float*>(h_scales_ws), y, signals, 2, stream);
 }
 

@@ -226,7 +226,8 @@ __global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_count
 }
 
 // Pass 3.  One wave per (token, 64-vector slice of its row): the slice-0
-// wave also publishes pos and row_src.  row_bytes: bytes of one x row (a
+// wave also publishes pos and row_src.  Without x_perm (a grouped GEMM that
+// gathers its token rows through row_src) only that wave runs per token.  row_bytes: bytes of one x row (a
 // multiple of 16); n_slices = ceil(row_bytes / 1024).
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, const float* __restrict__ x_s,
                                                  int row_bytes, int n_scales, int n_slices, int T, int K,
@@ -256,6 +257,7 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
         }
         dst_lds[wv][lane] = p;
     }
+    if (x_perm == nullptr) return;  // layout only: the grouped GEMM gathers the rows (uniform)
     // the copy loops below leave lanes idle, so the destinations are read
     // from the wave's LDS slice rather than shuffled from other lanes
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -348,8 +350,9 @@ static hipError_t dispatch_passes(const void* x, const float* x_scales, int row_
                               L.offsets, L.masked_m, tile_off, L.status, L.expert_load);
     err = hipGetLastError();
     if (err != hipSuccess || T == 0) return err;
-    const int n_scales = x_scales ? H / 128 : 0;
-    const int n_slices = (row_bytes + 16 * kWave - 1) / (16 * kWave);
+    // without x_perm only pos and row_src are published: one wave per token
+    const int n_scales = x_scales && x_perm ? H / 128 : 0;
+    const int n_slices = x_perm ? (row_bytes + 16 * kWave - 1) / (16 * kWave) : 1;
     const int64_t units = (int64_t)T * n_slices;
     k_scatter<<<(unsigned)((units + 3) / 4), 256, 0, s>>>(static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales,
                                                           n_slices, T, K, ids, L.n_local, chunk, chunk_counts,

@@ -120,8 +120,10 @@ struct KArgs {
     const int32_t* masked_m;
     const int32_t* tile_off;
     int n_local, Kdim, Nout;
-    const uint8_t* X;     // [rows, Kdim] layout rows
+    const uint8_t* X;     // [rows, Kdim] layout rows, or tokens read through gather
     const float* Xs;      // fp8: [rows, Kdim/128]
+    const int32_t* gather;  // NULL, or the layout's row_src: row r's operand is token gather[r] / gather_k
+    int gather_k;
     const uint8_t* Wa;    // [n_local, Nout, Kdim]  (W1, or W2)
     const uint8_t* Wb;    // [n_local, Nout, Kdim]  (W3 when gated)
     const float* Was;     // fp8: [n_local, Nout/128, Kdim/128]
@@ -173,12 +175,14 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
         brow[rt] = GATED ? a.Wb + grp * nks * M::BLK : nullptr;
     }
     const uint8_t* xrow[NCT];
+    int xr[NCT];  // the operand row (layout row, or gathered token) of each token tile
     bool xv[NCT];
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
         const int r = row0 + ct * 16 + (lane & 15);
         xv[ct] = r < row_end;
-        xrow[ct] = a.X + (size_t)(xv[ct] ? r : row0) * wstride;
+        xr[ct] = token_row(a.gather, a.gather_k, xv[ct] ? r : row0);
+        xrow[ct] = a.X + (size_t)xr[ct] * wstride;
     }
 
     f32x4_t accA[2][NCT], accB[2][NCT];
@@ -227,7 +231,7 @@ __global__ __launch_bounds__(256) void k_ffn(KArgs a) {
             const float sb_w = GATED ? wbs[kb] : 0.0f;
 #pragma unroll
             for (int ct = 0; ct < NCT; ++ct) {
-                const float sx = xv[ct] ? a.Xs[(size_t)(row0 + ct * 16 + (lane & 15)) * nkb + kb] : 0.0f;
+                const float sx = xv[ct] ? a.Xs[(size_t)xr[ct] * nkb + kb] : 0.0f;
                 const float fa = sx * sa_w, fb = sx * sb_w;
 #pragma unroll
                 for (int rt = 0; rt < 2; ++rt) {
@@ -393,9 +397,10 @@ __global__ __launch_bounds__(256) void k_ffn_skinny(KArgs a) {
     const uint8_t* xrow[NR];
 #pragma unroll
     for (int nr = 0; nr < NR; ++nr) {
-        xr[nr] = row0 + nr * 16 + (lane & 15);
-        xv[nr] = xr[nr] < row_end;
-        xrow[nr] = a.X + (size_t)(xv[nr] ? xr[nr] : row0) * wstride;
+        const int r = row0 + nr * 16 + (lane & 15);
+        xv[nr] = r < row_end;
+        xr[nr] = token_row(a.gather, a.gather_k, xv[nr] ? r : row0);  // the operand row
+        xrow[nr] = a.X + (size_t)xr[nr] * wstride;
     }
     // weights of an expert whose rows span several row tiles are read by
     // each of them: then cacheable loads, so that the sibling tiles (run
@@ -526,6 +531,8 @@ KArgs gate_up_args(const FfnCall& c) {
     g.Nout = c.I;
     g.X = static_cast<const uint8_t*>(c.x);
     g.Xs = c.x_s;
+    g.gather = c.gather;
+    g.gather_k = c.gather_k;
     g.Wa = static_cast<const uint8_t*>(c.W1);
     g.Wb = static_cast<const uint8_t*>(c.W3);
     g.Was = c.W1_s;
@@ -545,8 +552,9 @@ KArgs down_args(const FfnCall& c) {
     d.n_local = c.n_local;
     d.Kdim = c.I;  // down: Kdim = I, Nout = H, input h
     d.Nout = c.H;
-    d.X = static_cast<const uint8_t*>(c.h);
+    d.X = static_cast<const uint8_t*>(c.h);  // h is in layout order
     d.Xs = c.h_s;
+    d.gather = nullptr;
     d.Wa = static_cast<const uint8_t*>(c.W2);
     d.Wb = nullptr;
     d.Was = c.W2_s;

@@ -179,8 +179,10 @@ struct TArgs {
     const int32_t* masked_m;
     const int32_t* tile_off;  // BT = 128 prefix table
     int n_local, Kdim, Nout, n_tiles_max;
-    const uint8_t* X;
+    const uint8_t* X;        // layout rows, or tokens read through gather
     const float* Xs;
+    const int32_t* gather;   // NULL, or the layout's row_src: row r's operand is token gather[r] / gather_k
+    int gather_k;
     const uint8_t* Wa;
     const uint8_t* Wb;
     const float* Was;
@@ -247,14 +249,36 @@ struct Ring {
     float* w;    // fp8: [NW waves][2][STEPS] the chunk's weight block scales of each wave (W1 / W2, W3)
 };
 
+// The operand rows this lane stages, found once per workgroup: rows past
+// the tile's valid rows re-read the last valid row (in bounds, never
+// stored); with a gather, each row's token.  xr[i]: the 16 bytes of x-load
+// i (see stage_chunk); sr: fp8, the activation scales of row 16 wv + l / SPB.
+template <int CB>
+struct StageRows {
+    static constexpr int XLOADS = TB * CB / 1024 / NW, PPR = CB / 16, SPB = CB / 128;
+    int xr[XLOADS];
+    int sr;
+    __device__ StageRows(const TArgs& a, int row0, int nvalid, int wv, int lane) {
+#pragma unroll
+        for (int i = 0; i < XLOADS; ++i) {
+            const int r = (wv * XLOADS + i) * (1024 / CB) + lane / PPR;
+            xr[i] = token_row(a.gather, a.gather_k, row0 + (r < nvalid ? r : nvalid - 1));
+        }
+        sr = 0;
+        if constexpr (SPB > 0) {
+            const int r = wv * 16 + (lane % (16 * SPB)) / SPB;
+            sr = token_row(a.gather, a.gather_k, row0 + (r < nvalid ? r : nvalid - 1));
+        }
+    }
+};
+
 // Request chunk kc of the tile's token rows: 128 * CB / 1024 / NW direct KiB
-// loads per wave (rows past the tile's valid rows re-read the last valid row:
-// in bounds, never stored); fp8: one load of the chunk's activation scales of
-// 16 rows per wave.
+// loads per wave; fp8: one load of the chunk's activation scales of 16 rows
+// per wave.
 template <int DT, int CB>
-__device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, int row0, int nvalid, int kc,
-                                            const Ring& ring, int wv, int lane) {
-    constexpr int XLOADS = TB * CB / 1024 / NW, SPB = CB / 128;
+__device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int nkb, const StageRows<CB>& rows,
+                                            int kc, const Ring& ring, int wv, int lane) {
+    constexpr int XLOADS = StageRows<CB>::XLOADS, SPB = CB / 128;
     constexpr int PPR = CB / 16;  // 16-byte pieces per row
     static_assert(XLOADS >= 1 && 1024 % CB == 0 && XLOADS * NW * 1024 == TB * CB, "chunk shape");
 #pragma unroll
@@ -262,17 +286,14 @@ __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int 
         const int q = wv * XLOADS + i;               // LDS bytes [q*1024, q*1024+1024)
         const int r = q * (1024 / CB) + lane / PPR;  // tile row of this lane's 16 bytes
         const int c = piece_slot<CB>(r, lane % PPR);  // source piece of this lane's slot
-        const int rr = r < nvalid ? r : nvalid - 1;
-        const uint8_t* src = a.X + (size_t)(row0 + rr) * xstride + (size_t)kc * CB + c * 16;
+        const uint8_t* src = a.X + (size_t)rows.xr[i] * xstride + (size_t)kc * CB + c * 16;
         dma16<DT == RDG_FP8_E4M3>(src, ring.x + q * 1024);
     }
     if constexpr (DT == RDG_FP8_E4M3) {
         // lanes 0..16*SPB-1 of wave w: row 16w + l/SPB, scale block SPB*kc + l%SPB
         static_assert(TB == 16 * NW && SPB * 16 <= 64, "one load of scales per wave");
         const int l = lane % (16 * SPB);
-        const int r = wv * 16 + l / SPB;
-        const int rr = r < nvalid ? r : nvalid - 1;
-        const float* src = a.Xs + (size_t)(row0 + rr) * nkb + SPB * kc + l % SPB;
+        const float* src = a.Xs + (size_t)rows.sr * nkb + SPB * kc + l % SPB;
         if (lane < 16 * SPB)
             dma4(src, ring.s + wv * 16 * SPB);
     }
@@ -347,6 +368,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     const int nks = a.Kdim / O::KS;
     const int nkb = a.Kdim / 128;
     const int nchunks = (int)(xstride / CB);
+    const StageRows<CB> srows(a, row0, nvalid, wv, lane);
 
     // weight tile rt: rows fw + 16 (rt % NOT) of W1 (gated, rt < NOT) or W3
     // (gated, rt >= NOT) or W2 (down)
@@ -464,7 +486,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // [16w, 16w+16).
     auto main_loop2 = [&](auto nv) {
         constexpr int NV = decltype(nv)::value;
-        if (wv < NV) stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+        if (wv < NV) stage_chunk<DT, CB>(a, xstride, nkb, srows, 0, ring[0], wv, lane);
         request_w(0, w[0], ring[0]);
         for (int kc0 = 0; kc0 < nchunks; kc0 += 2) {
 #pragma unroll
@@ -478,7 +500,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 lds_barrier();
                 if (kc + 1 < nchunks) {
                     if (wv < NV)
-                        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, kc + 1, ring[(j + 1) % 2], wv, lane);
+                        stage_chunk<DT, CB>(a, xstride, nkb, srows, kc + 1, ring[(j + 1) % 2], wv, lane);
                     request_w(kc + 1, w[(j + 1) % 2], ring[(j + 1) % 2]);
                 }
                 compute(ring[j], w[j], nv);
@@ -497,10 +519,10 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     // register set).  The last loads are drained before the epilogue.
     auto main_loop3 = [&](auto nv) {
         constexpr int LPC = TB * CB / 1024 / NW + S * NRT;  // vector-memory loads per chunk and wave
-        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, 0, ring[0], wv, lane);
+        stage_chunk<DT, CB>(a, xstride, nkb, srows, 0, ring[0], wv, lane);
         request_w(0, w[0], ring[0]);
         const int c1 = nchunks > 1 ? 1 : 0;
-        stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, c1, ring[1], wv, lane);
+        stage_chunk<DT, CB>(a, xstride, nkb, srows, c1, ring[1], wv, lane);
         request_w(c1, w[1], ring[1]);
         for (int kc0 = 0; kc0 < nchunks; kc0 += 3) {
 #pragma unroll
@@ -509,7 +531,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 __builtin_amdgcn_s_waitcnt(vmcnt_imm<LPC>());
                 lds_barrier();
                 const int kn = kc + 2 < nchunks ? kc + 2 : nchunks - 1;
-                stage_chunk<DT, CB>(a, xstride, nkb, row0, nvalid, kn, ring[(j + 2) % 3], wv, lane);
+                stage_chunk<DT, CB>(a, xstride, nkb, srows, kn, ring[(j + 2) % 3], wv, lane);
                 request_w(kn, w[(j + 2) % 3], ring[(j + 2) % 3]);
                 if (kc < nchunks) compute(ring[j], w[j], nv);
             }
@@ -610,7 +632,7 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
     dim3 block(NW * 64);
     if (c.stages & 1) {
         TArgs g{c.offsets, c.masked_m, c.tile_off, c.n_local, c.H, c.I, c.n_tiles_max,
-                static_cast<const uint8_t*>(c.x), c.x_s, static_cast<const uint8_t*>(c.W1),
+                static_cast<const uint8_t*>(c.x), c.x_s, c.gather, c.gather_k, static_cast<const uint8_t*>(c.W1),
                 static_cast<const uint8_t*>(c.W3), c.W1_s, c.W3_s, static_cast<uint8_t*>(c.h), c.h_s, nullptr};
         k_ffn_tiled<DT, true, false, PW2, WIDE><<<dim3(c.n_tiles_max, c.I / (PANEL / 2)), block, 0, s>>>(g);
         hipError_t err = hipGetLastError();
@@ -618,8 +640,8 @@ hipError_t launch_dt(const FfnCall& c, hipStream_t s) {
     }
     if (c.stages & 2) {
         TArgs d{c.offsets, c.masked_m, c.tile_off, c.n_local, c.I, c.H, c.n_tiles_max,
-                static_cast<const uint8_t*>(c.h), c.h_s, static_cast<const uint8_t*>(c.W2), nullptr, c.W2_s,
-                nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
+                static_cast<const uint8_t*>(c.h), c.h_s, nullptr, 0, static_cast<const uint8_t*>(c.W2), nullptr,
+                c.W2_s, nullptr, static_cast<uint8_t*>(c.y), nullptr, c.signals};
         if (c.signals)
             k_ffn_tiled<DT, false, true, PW2, WIDE><<<dim3(round8(c.H / PANEL), c.n_tiles_max), block, 0, s>>>(d);
         else

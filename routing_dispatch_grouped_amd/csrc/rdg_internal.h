@@ -92,6 +92,14 @@ __device__ __forceinline__ float wave_max_f32(float x) {
 
 __device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & (kWave - 1)); }
 
+// The row of the gate/up GEMM's token operand that holds layout row r: r
+// itself when the dispatch permuted the rows (x_perm), or, when the GEMM
+// gathers from the unpermuted tokens, the token t of row_src[r] = t*K + k.
+// gather is a kernel argument, so the branch is uniform.
+__device__ __forceinline__ int token_row(const int32_t* gather, int gather_k, int r) {
+    return gather ? gather[r] / gather_k : r;
+}
+
 // First error wins: code into st[0] (if still 0), then its detail into st[1].
 __device__ __forceinline__ void set_status(int32_t* st, int code, int detail) {
     if (st != nullptr && atomicCAS(st, 0, code) == 0) atomicExch(st + 1, detail);
@@ -190,6 +198,8 @@ struct FfnCall {
     int skinny_nr;  // > 0: skinny kernel with bt = 16 * skinny_nr (weight streaming)
     int dtype, H, I;
     const void *x, *W1, *W3, *W2;
+    const int32_t* gather;  // NULL: x holds layout rows; else x holds tokens and layout row r reads
+    int gather_k;           // token gather[r] / gather_k (gather = the layout's row_src, gather_k = K)
     const float *x_s, *W1_s, *W3_s, *W2_s;
     void* h;
     float* h_s;

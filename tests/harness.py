@@ -117,9 +117,11 @@ def quantize_act(x, pow2=False):
 
 
 def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max=0, shared_out=None,
-               signals=False, max_blocks=0, concurrent=False, timeout_us=2_000_000):
+               signals=False, max_blocks=0, concurrent=False, timeout_us=2_000_000, gather=False):
     """dispatch -> grouped FFN -> combine on the device.  Returns a dict of
-    device tensors (layout, x_perm, h, y, out)."""
+    device tensors (layout, x_perm, h, y, out).  gather: the dispatch builds
+    the layout only and the grouped FFN reads the token rows through it
+    (rdg_grouped_ffn_gather; x_perm is then None)."""
     m = rdg()
     dt = dt_code(cfg)
     T, H = x.shape
@@ -128,9 +130,22 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
     n_local = experts.W1.shape[0]
     L = m.Layout(kind, n_local, T, K, x.device, block_m=block_m, m_max=m_max)
     sdt = torch_dtype(dt)
-    x_perm = torch.empty((L.m_cap, H), dtype=sdt, device=x.device)
-    x_perm_s = torch.empty((L.m_cap, H // 128), dtype=torch.float32, device=x.device) if x_s is not None else None
-    m.rdg_dispatch(x, x_s, dt, local_ids, L, x_perm, x_perm_s)
+    if gather:
+        x_perm = x_perm_s = None
+        m.rdg_dispatch(x, None, dt, local_ids, L, None, None)
+    else:
+        x_perm = torch.empty((L.m_cap, H), dtype=sdt, device=x.device)
+        x_perm_s = (torch.empty((L.m_cap, H // 128), dtype=torch.float32, device=x.device)
+                    if x_s is not None else None)
+        m.rdg_dispatch(x, x_s, dt, local_ids, L, x_perm, x_perm_s)
+
+    def ffn(stream=None):
+        if gather:
+            m.rdg_grouped_ffn_gather(L, dt, H, I, x, x_s, K, experts.W1, experts.W3, experts.W2, experts.s1,
+                                     experts.s3, experts.s2, h, h_s, y, sig, stream=stream)
+        else:
+            m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
+                              experts.s3, experts.s2, h, h_s, y, sig, stream=stream)
     h = torch.empty((L.m_cap, I), dtype=sdt, device=x.device)
     h_s = torch.empty((L.m_cap, I // 128), dtype=torch.float32, device=x.device) if is_fp8(cfg) else None
     ydt = torch.float32 if dt == m.RDG_F32 else torch.bfloat16
@@ -156,15 +171,13 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
         s_gemm = torch.cuda.current_stream()
         s_comb = torch.cuda.Stream()
         s_comb.wait_stream(s_gemm)  # combine starts after dispatch; it then overlaps the GEMMs
-        m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
-                          experts.s3, experts.s2, h, h_s, y, sig, stream=s_gemm)
+        ffn(stream=s_gemm)
         with torch.cuda.stream(s_comb):
             m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0,
                           thr, timeout_us, max_blocks, stream=s_comb)
         s_gemm.wait_stream(s_comb)
     else:
-        m.rdg_grouped_ffn(L, dt, H, I, x_perm, x_perm_s, experts.W1, experts.W3, experts.W2, experts.s1,
-                          experts.s3, experts.s2, h, h_s, y, sig)
+        ffn()
         m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0, thr,
                       timeout_us, max_blocks)
     return dict(L=L, x_perm=x_perm, x_perm_s=x_perm_s, h=h, h_s=h_s, y=y, out=out, signals=sig, threshold=thr,

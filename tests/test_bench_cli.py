@@ -23,7 +23,7 @@ def test_defaults(monkeypatch):
     monkeypatch.setattr(sys, "argv", ["bench.py"])
     a = bench.parse()
     assert (a.gpus, a.steps, a.warmup, a.workload, a.cpu_tokens) == (1, 20, 5, "prefill_bf16", None)
-    assert a.summary == "auto" and a.eplb_replicas is None
+    assert a.summary == "auto" and a.eplb_replicas is None and a.payload == "gather"
     assert not (a.graph or a.ue8m0 or a.tbo or a.calibrate_copy)
     assert bench.CPU_TOKENS["prefill_bf16"] > 0 and set(bench.CPU_TOKENS) == set(bench.ALL_WORKLOADS)
 
@@ -44,6 +44,9 @@ def test_layer_bytes_decode():
     shared = T * (H + I) * 2 + T * (I + H) * 2
     combine = R * H * 2 + T * H * 2 + T * H * 2        # routed rows, shared output, result
     assert bench.layer_bytes(cfg, T, R, A, 2) == weights + route + permute + routed + shared + combine
+    # gathering: the dispatch only publishes pos [T*K] and row_src [R]
+    assert bench.layer_bytes(cfg, T, R, A, 2, gather=True) == (weights + route + T * K * 4 + R * 4 + routed + shared
+                                                               + combine)
 
 
 def test_layer_bytes_fp8_scales():

@@ -64,7 +64,7 @@ def _cover(ids, n_local, n, seed, tile=128):
     return np.array(sorted(keep), dtype=np.int64)
 
 
-def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
+def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0, gather=False):
     """Workloads where this GPU holds every expert (the tiny, decode and prefill layers)."""
     m = rdg()
     dt = dt_code(cfg)
@@ -84,7 +84,8 @@ def _full_layer(cfg, B, kind, block_m=128, m_max=0, n_sample=None, seed=0):
     experts = ExpertSet(cfg, range(N))
     shared = ExpertSet(cfg, [0], shared=True) if cfg["shared_I"] else None
     sh_out = run_shared(cfg, x, x_s, shared) if shared else None
-    r = run_routed(cfg, x, x_s, ids, w, experts, kind, block_m=block_m, m_max=m_max, shared_out=sh_out)
+    r = run_routed(cfg, x, x_s, ids, w, experts, kind, block_m=block_m, m_max=m_max, shared_out=sh_out,
+                   gather=gather)
     st = m.rdg_check_status(r["L"])
     ref_l = oracle.layout(ri, N, kind, block_m=block_m, m_max=m_max)
     assert st == (ref_l["status"], ref_l["detail"])
