@@ -104,8 +104,17 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ ids, i
     for (int e = lane; e < n_local; e += kWave) chunk_counts[(size_t)c * n_local + e] = cnt[e];
 }
 
-// Exclusive scan over a 1024-thread workgroup (16 waves).
-__device__ int block_exclusive_scan(int v, int* lds16, int* total) {
+// Pass 2 runs as one workgroup of 256 threads (four waves, one per SIMD):
+// small enough in registers (about 60 per lane) to start beside a
+// workgroup of the 128-row GEMM, which leaves 96 of each SIMD's 512
+// registers free, so that a GEMM running on another stream (the shared
+// expert) does not hold up the dispatch.
+constexpr int kScanThreads = 256;
+constexpr int kScanEPT = 4;  // experts per thread (n_local <= 1024)
+static_assert(kScanThreads * kScanEPT >= 1024 && kScanEPT == 4, "the 16-byte loads of k_scan hold four experts");
+
+// Exclusive scan over the pass-2 workgroup (4 waves); lds4: 4 ints.
+__device__ int block_exclusive_scan(int v, int* lds4, int* total) {
     const int lane = lane_id(), wv = threadIdx.x / kWave;
     int x = v;
 #pragma unroll
@@ -113,115 +122,171 @@ __device__ int block_exclusive_scan(int v, int* lds16, int* total) {
         int y = __shfl_up(x, off);
         if (lane >= off) x += y;
     }
-    if (lane == kWave - 1) lds16[wv] = x;
+    if (lane == kWave - 1) lds4[wv] = x;
     __syncthreads();
-    if (wv == 0) {
-        int w = lane < 16 ? lds16[lane] : 0;
+    int before = 0, tot = 0;
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            int y = __shfl_up(w, off);
-            if (lane >= off) w += y;
-        }
-        if (lane < 16) lds16[16 + lane] = w;  // inclusive wave totals
+    for (int w = 0; w < kScanThreads / kWave; ++w) {
+        const int t = lds4[w];
+        before += w < wv ? t : 0;
+        tot += t;
     }
-    __syncthreads();
-    int before = wv > 0 ? lds16[16 + wv - 1] : 0;
-    int tot = lds16[16 + 15];
     __syncthreads();
     *total = tot;
     return before + x - v;
 }
 
-__device__ int block_max(int v, int* lds16) {
+__device__ int block_max(int v, int* lds4) {
     const int lane = lane_id(), wv = threadIdx.x / kWave;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off));
-    if (lane == 0) lds16[wv] = v;
+    if (lane == 0) lds4[wv] = v;
     __syncthreads();
-    int m = lds16[0];
-    for (int i = 1; i < 16; ++i) m = max(m, lds16[i]);
+    int m = lds4[0];
+#pragma unroll
+    for (int w = 1; w < kScanThreads / kWave; ++w) m = max(m, lds4[w]);
     __syncthreads();
     return m;
 }
 
-// Pass 2.  One workgroup of 1024 threads; thread e owns expert e (n_local <= 1024).
-__global__ __launch_bounds__(1024) void k_scan(int32_t* __restrict__ chunk_counts, int n_chunks, int n_local,
-                                               int kind, int block_m, int m_max, int m_cap,
-                                               int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                                               int32_t* __restrict__ masked_m, int32_t* __restrict__ tile_off,
-                                               int32_t* __restrict__ status, int64_t* __restrict__ expert_load) {
-    __shared__ int lds[32];
+// Exclusive scan of the values v[i] of experts kScanEPT*j + i (thread j, in
+// expert order): each expert's offset, and the total.
+__device__ void experts_exclusive_scan(const int (&v)[kScanEPT], int (&out)[kScanEPT], int* lds4, int* total) {
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kScanEPT; ++i) {
+        out[i] = sum;
+        sum += v[i];
+    }
+    const int base = block_exclusive_scan(sum, lds4, total);
+#pragma unroll
+    for (int i = 0; i < kScanEPT; ++i) out[i] += base;
+}
+
+// Pass 2.  Thread j owns experts kScanEPT*j .. +kScanEPT-1: the exclusive
+// scan of each expert's per-chunk counts over the chunks (each chunk's base
+// row inside the expert), the expert's count, then offsets, masked_m, the
+// status and the row-tile tables, all scans in expert order.
+__global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ chunk_counts, int n_chunks,
+                                                       int n_local, int kind, int block_m, int m_max, int m_cap,
+                                                       int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ masked_m,
+                                                       int32_t* __restrict__ tile_off, int32_t* __restrict__ status,
+                                                       int64_t* __restrict__ expert_load) {
+    __shared__ int lds[4];
     __shared__ int cells[1024];
-    const int e = threadIdx.x;
-    const bool act = e < n_local;
-    int run = 0;
+    const int j = threadIdx.x;
+    const int e0 = j * kScanEPT;
+    int run[kScanEPT];
+#pragma unroll
+    for (int i = 0; i < kScanEPT; ++i) run[i] = 0;
     const int64_t n_cells = (int64_t)n_local * n_chunks;
     if (n_cells <= 1024) {
-        // every (chunk, expert) count in one round of loads, one per thread;
-        // each expert's thread scans its column from LDS
-        if (e < n_cells) cells[e] = chunk_counts[e];
+        // every (chunk, expert) count in one round of loads; each expert's
+        // column scanned from LDS
+        for (int c = j; c < n_cells; c += kScanThreads) cells[c] = chunk_counts[c];
         __syncthreads();
-        if (act) {
+#pragma unroll
+        for (int i = 0; i < kScanEPT; ++i) {
+            if (e0 + i >= n_local) continue;
             for (int c = 0; c < n_chunks; ++c) {
-                const int v = cells[c * n_local + e];
-                cells[c * n_local + e] = run;
-                run += v;
+                const int v = cells[c * n_local + e0 + i];
+                cells[c * n_local + e0 + i] = run[i];
+                run[i] += v;
             }
         }
         __syncthreads();
-        if (e < n_cells) chunk_counts[e] = cells[e];
-    } else if (act) {
-        int c = 0;
-        for (; c + 8 <= n_chunks; c += 8) {  // issue eight independent loads, then scan them
-            int v[8];
+        for (int c = j; c < n_cells; c += kScanThreads) chunk_counts[c] = cells[c];
+    } else if (e0 < n_local) {
+        if (n_local % kScanEPT == 0) {
+            // a row of the chunk table is n_local ints from a 256-byte aligned
+            // base: the thread's four experts are one aligned 16-byte vector
+            int c = 0;
+            for (; c + 8 <= n_chunks; c += 8) {  // eight independent loads, then their scans
+                int4 v[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) v[j] = chunk_counts[(size_t)(c + j) * n_local + e];
+                for (int u = 0; u < 8; ++u)
+                    v[u] = *reinterpret_cast<const int4*>(chunk_counts + (size_t)(c + u) * n_local + e0);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                chunk_counts[(size_t)(c + j) * n_local + e] = run;
-                run += v[j];
+                for (int u = 0; u < 8; ++u) {
+                    *reinterpret_cast<int4*>(chunk_counts + (size_t)(c + u) * n_local + e0) =
+                        make_int4(run[0], run[1], run[2], run[3]);
+                    run[0] += v[u].x;
+                    run[1] += v[u].y;
+                    run[2] += v[u].z;
+                    run[3] += v[u].w;
+                }
+            }
+            for (; c < n_chunks; ++c) {
+                int4* p = reinterpret_cast<int4*>(chunk_counts + (size_t)c * n_local + e0);
+                const int4 v = *p;
+                *p = make_int4(run[0], run[1], run[2], run[3]);
+                run[0] += v.x;
+                run[1] += v.y;
+                run[2] += v.z;
+                run[3] += v.w;
+            }
+        } else {
+            for (int c = 0; c < n_chunks; ++c) {
+#pragma unroll
+                for (int i = 0; i < kScanEPT; ++i) {
+                    if (e0 + i >= n_local) continue;
+                    int32_t* p = chunk_counts + (size_t)c * n_local + e0 + i;
+                    const int v = *p;
+                    *p = run[i];
+                    run[i] += v;
+                }
             }
         }
-        for (; c < n_chunks; ++c) {
-            int32_t* p = chunk_counts + (size_t)c * n_local + e;
-            int v = *p;
-            *p = run;
-            run += v;
+    }
+    int seg[kScanEPT], off[kScanEPT], keep[kScanEPT];
+    int worst = 0;
+#pragma unroll
+    for (int i = 0; i < kScanEPT; ++i) {
+        const int e = e0 + i;
+        const bool act = e < n_local;
+        if (act) {
+            counts[e] = run[i];
+            // the expert-load recorder: routed rows before any capacity drop
+            if (expert_load != nullptr)
+                atomicAdd(reinterpret_cast<unsigned long long*>(expert_load + e), (unsigned long long)run[i]);
+        }
+        seg[i] = !act ? 0 : kind == RDG_MASKED ? m_max : (run[i] + block_m - 1) / block_m * block_m;
+        worst = act && run[i] > worst ? run[i] : worst;
+    }
+    int total;
+    experts_exclusive_scan(seg, off, lds, &total);
+#pragma unroll
+    for (int i = 0; i < kScanEPT; ++i) {
+        int k = run[i];
+        if (kind == RDG_MASKED && k > m_max) k = m_max;
+        if (kind == RDG_CONTIGUOUS) {
+            int room = m_cap - off[i];
+            if (room < 0) room = 0;
+            if (k > room) k = room;
+        }
+        keep[i] = e0 + i < n_local ? k : 0;
+        if (e0 + i < n_local) {
+            offsets[e0 + i] = off[i];
+            masked_m[e0 + i] = keep[i];
         }
     }
-    if (act) {
-        counts[e] = run;
-        // the expert-load recorder: routed rows before any capacity drop
-        if (expert_load != nullptr)
-            atomicAdd(reinterpret_cast<unsigned long long*>(expert_load + e), (unsigned long long)run);
-    }
-    int seg = 0;
-    if (act) seg = kind == RDG_MASKED ? m_max : (run + block_m - 1) / block_m * block_m;
-    int total;
-    int off = block_exclusive_scan(seg, lds, &total);
-    int keep = run;
-    if (kind == RDG_MASKED && keep > m_max) keep = m_max;
-    if (kind == RDG_CONTIGUOUS) {
-        int room = m_cap - off;
-        if (room < 0) room = 0;
-        if (keep > room) keep = room;
-    }
-    if (act) {
-        offsets[e] = off;
-        masked_m[e] = keep;
-    }
-    if (e == 0) offsets[n_local] = total;
-    int worst = block_max(act ? run : 0, lds);
-    if (e == 0) {
+    if (j == 0) offsets[n_local] = total;
+    worst = block_max(worst, lds);
+    if (j == 0) {
         if (kind == RDG_MASKED && worst > m_max) set_status(status, RDG_ECAPACITY, worst);
         if (kind == RDG_CONTIGUOUS && total > m_cap) set_status(status, RDG_ECAPACITY, total);
     }
     for (int b = 0; b < kNumBT; ++b) {
-        int nt = act ? (keep + kBT[b] - 1) / kBT[b] : 0;
+        int nt[kScanEPT], to[kScanEPT];
+#pragma unroll
+        for (int i = 0; i < kScanEPT; ++i) nt[i] = (keep[i] + kBT[b] - 1) / kBT[b];
         int tt;
-        int to = block_exclusive_scan(nt, lds, &tt);
-        if (act) tile_off[b * (n_local + 1) + e] = to;
-        if (e == 0) tile_off[b * (n_local + 1) + n_local] = tt;
+        experts_exclusive_scan(nt, to, lds, &tt);
+#pragma unroll
+        for (int i = 0; i < kScanEPT; ++i)
+            if (e0 + i < n_local) tile_off[b * (n_local + 1) + e0 + i] = to[i];
+        if (j == 0) tile_off[b * (n_local + 1) + n_local] = tt;
     }
 }
 
@@ -346,7 +411,7 @@ static hipError_t dispatch_passes(const void* x, const float* x_scales, int row_
                                                                    L.status);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    k_scan<<<1, 1024, 0, s>>>(chunk_counts, n_chunks, L.n_local, L.kind, L.block_m, L.m_max, L.m_cap, L.counts,
+    k_scan<<<1, kScanThreads, 0, s>>>(chunk_counts, n_chunks, L.n_local, L.kind, L.block_m, L.m_max, L.m_cap, L.counts,
                               L.offsets, L.masked_m, tile_off, L.status, L.expert_load);
     err = hipGetLastError();
     if (err != hipSuccess || T == 0) return err;

@@ -82,6 +82,21 @@ def test_masked_and_capacity(T, K, E, m_max):
     assert np.array_equal(np_of(xp)[filled], np_of(x)[rs[filled] // K])
 
 
+@pytest.mark.parametrize("T,K,E,kind,m_max", [(4096, 8, 256, 0, 0), (1000, 8, 37, 0, 0), (16384, 8, 1024, 0, 0),
+                                                (128, 8, 32, 1, 7), (0, 8, 4, 0, 0)])
+def test_layout_only(T, K, E, kind, m_max):
+    # x_perm = NULL: the same layout (for a grouped GEMM that gathers the
+    # rows through row_src), nothing copied, x not read
+    m = rdg()
+    ids = _ids(np.random.default_rng([T, K, E, 5]), T, K, E, skew=True, holes=0.1)
+    L = m.Layout(kind, E, T, K, DEV, block_m=128, m_max=m_max)
+    x = torch.empty((T, 256), dtype=torch.bfloat16, device=DEV)
+    m.rdg_dispatch(x, None, m.RDG_BF16, torch.from_numpy(ids).to(DEV), L, None, None)
+    ref = oracle.layout(ids, E, oracle.MASKED if kind else oracle.CONTIGUOUS, block_m=128, m_max=m_max)
+    assert m.rdg_check_status(L) == (ref["status"], ref["detail"])
+    check_layout(L, ref, ids.shape)
+
+
 def test_contiguous_overflow():
     m = rdg()
     ids = _ids(np.random.default_rng(3), 300, 8, 20)
