@@ -90,15 +90,24 @@ def parse():
 # Files whose contents determine the dominant kernel's memory traffic (the
 # kernel, its device helpers and the packed weight layout); the committed
 # counter figures apply only while their hash is unchanged.
-TRAFFIC_SOURCES = ["routing_dispatch_grouped_amd/csrc/ffn.hip", "routing_dispatch_grouped_amd/csrc/ffn_tiled.hip",
-                   "routing_dispatch_grouped_amd/csrc/rdg_internal.h", "routing_dispatch_grouped_amd/csrc/pack.hip",
-                   "routing_dispatch_grouped_amd/csrc/abi.hip"]
+# the sources that decide the dominant kernel's memory traffic: its kernel
+# file (the 16-64-row kernels for the decode and tiny layers, the 128-row
+# tiles for the prefill layers and the rank shares), the shared helpers, the
+# weight packing, and the kernel choice in the C ABI
+TRAFFIC_COMMON = ["routing_dispatch_grouped_amd/csrc/rdg_internal.h", "routing_dispatch_grouped_amd/csrc/pack.hip",
+                  "routing_dispatch_grouped_amd/csrc/abi.hip"]
+TRAFFIC_KERNEL = {"decode_bf16": "routing_dispatch_grouped_amd/csrc/ffn.hip",
+                  "tiny_fp32": "routing_dispatch_grouped_amd/csrc/ffn.hip"}
 
 
-def source_hash():
+def traffic_sources(workload):
+    return [TRAFFIC_KERNEL.get(workload, "routing_dispatch_grouped_amd/csrc/ffn_tiled.hip")] + TRAFFIC_COMMON
+
+
+def source_hash(workload):
     import hashlib
     h = hashlib.sha256()
-    for f in TRAFFIC_SOURCES:
+    for f in traffic_sources(workload):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -115,7 +124,7 @@ def measured_traffic(workload):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_hash") != source_hash():
+    if kv.get("source_hash") != source_hash(workload):
         return None
     try:
         return float(kv["traffic_bytes_per_launch"])
@@ -589,7 +598,7 @@ def _roofline(cfg, active, rows, gate_ms, workload):
             "achieved": gbps if hbm_bound else tflops, "peak": HBM_PEAK_GBPS if hbm_bound else peak_f,
             "unit": "GB/s" if hbm_bound else "TFLOP/s", "frac": hbm_frac if hbm_bound else mfma_frac,
             "traffic": measured_traffic(workload), "avg_ms": gate_ms, "algorithmic_bytes": gate_bytes,
-            "algorithmic_flops": gate_flops, "source_hash": source_hash(),
+            "algorithmic_flops": gate_flops, "source_hash": source_hash(workload),
             "hbm_frac": hbm_frac, "mfma_frac": mfma_frac}
 
 
