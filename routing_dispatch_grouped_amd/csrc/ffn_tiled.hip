@@ -305,6 +305,100 @@ __device__ __forceinline__ void stage_chunk(const TArgs& a, size_t xstride, int 
     }
 }
 
+// Work order of the plain down GEMM (a tile's output columns in panels of
+// PANEL, gridDim.y panels).  Row tiles of experts with several tiles ("busy")
+// keep the order above: XCD x runs a contiguous share of the (panel, tile)
+// pairs, panel-major, so one weight panel serves consecutive row tiles from
+// its L2.  The tile of an expert with one tile has no sibling to share its
+// weights with, but every panel of it reads the same h rows (a quarter of
+// its bytes at I = 2048): its panels run back to back on one XCD, which then
+// fetches those rows once instead of every XCD fetching them.  Each XCD's
+// busy and one-tile items are interleaved in proportion (busy items alone
+// leave HBM idle, one-tile items alone the matrix cores), and the XCDs get
+// equal shares of both.  On the prefill layer's down GEMM: 1.77 -> 1.69 ms
+// (balanced layer 1.81 -> 1.66 ms); the gate/up GEMM, whose tokens are 6% of
+// a one-tile expert's bytes, was slower this way (3.03 -> 3.10 ms) and keeps
+// the plain order, and so does the fp8 down GEMM (the decode rank share's
+// step 0.158 -> 0.164 ms this way: its 308 workgroups need a second round).
+// Returns false (plain order) when some XCD would get more items than
+// workgroups; sets tile = -1 for a workgroup with no item.
+__device__ bool down_split(const TArgs& a, int& fb, int& tile) {
+    const int gx = a.n_tiles_max, gy = gridDim.y, total = gx * gy;
+    const int b = blockIdx.y * gx + blockIdx.x;
+    const int xcd = b % 8, q8 = total / 8, r8 = total % 8;
+    // exclusive prefixes over the experts of their busy tiles and of their
+    // one-tile counts (n_local <= 1024), built by the first wave
+    __shared__ int s_busy[1025], s_one[1025];
+    if (threadIdx.x < kWave) {
+        const int l = threadIdx.x, per = (a.n_local + kWave - 1) / kWave;
+        const int e0 = l * per, e1 = e0 + per < a.n_local ? e0 + per : a.n_local;
+        int bs = 0, os = 0;
+        for (int e = e0; e < e1; ++e) {
+            const int nt = a.tile_off[e + 1] - a.tile_off[e];
+            bs += nt >= 2 ? nt : 0;
+            os += nt == 1 ? 1 : 0;
+        }
+        int bx = bs, ox = os;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const int y = __shfl_up(bx, off), z = __shfl_up(ox, off);
+            if (l >= off) {
+                bx += y;
+                ox += z;
+            }
+        }
+        int bb = bx - bs, ob = ox - os;
+        for (int e = e0; e < e1; ++e) {
+            s_busy[e] = bb;
+            s_one[e] = ob;
+            const int nt = a.tile_off[e + 1] - a.tile_off[e];
+            bb += nt >= 2 ? nt : 0;
+            ob += nt == 1 ? 1 : 0;
+        }
+        if (l == kWave - 1) {
+            s_busy[a.n_local] = bx;
+            s_one[a.n_local] = ox;
+        }
+    }
+    __syncthreads();
+    const int NB = s_busy[a.n_local], NO = s_one[a.n_local];
+    const int busy_items = NB * gy, bq = busy_items / 8, br = busy_items % 8;
+    const int oq = NO / 8, orr = NO % 8;
+    for (int x = 0; x < 8; ++x)  // every XCD's items must fit its workgroups
+        if (bq + (x < br ? 1 : 0) + (oq + (x < orr ? 1 : 0)) * gy > q8 + (x < r8 ? 1 : 0)) return false;
+    const int busy_n = bq + (xcd < br ? 1 : 0), busy_start = xcd * bq + (xcd < br ? xcd : br);
+    const int one_n = oq + (xcd < orr ? 1 : 0), one_start = xcd * oq + (xcd < orr ? xcd : orr);
+    const int n_x = busy_n + one_n * gy, pos = b / 8;
+    tile = -1;
+    if (pos >= n_x) return true;
+    // item pos of the XCD is busy item floor(pos * busy_n / n_x) when that
+    // count steps at pos, else one-tile item pos - (busy items before it)
+    const int b0 = (int)((int64_t)pos * busy_n / n_x), b1 = (int)((int64_t)(pos + 1) * busy_n / n_x);
+    int lo = 0, hi = a.n_local;
+    if (b1 > b0) {
+        const int item = busy_start + b0;
+        fb = item / NB;
+        const int h = item % NB;
+        while (hi - lo > 1) {  // the last expert whose busy prefix is <= h
+            const int mid = (lo + hi) >> 1;
+            if (s_busy[mid] <= h) lo = mid;
+            else hi = mid;
+        }
+        tile = a.tile_off[lo] + (h - s_busy[lo]);
+    } else {
+        const int j = pos - b0;
+        const int c = one_start + j / gy;
+        fb = j % gy;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_one[mid] <= c) lo = mid;
+            else hi = mid;
+        }
+        tile = a.tile_off[lo];
+    }
+    return true;
+}
+
 // PW2 (fp8 with power-of-two block scales): the scales go into the scaled
 // MFMA as 8-bit exponents and the matrix core accumulates across blocks; no
 // per-block promotion.  WIDE: see TShape.
@@ -340,7 +434,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         fb = blockIdx.x;
         tile = blockIdx.y;
         if (fb * COLS >= a.Nout) return;  // padding workgroup (uniform)
-    } else {
+    } else if (GATED || FP8 || !down_split(a, fb, tile)) {
         // XCD-aware renumbering: hardware block b runs on XCD b % 8, which
         // gets ceil((total - x) / 8) blocks; give XCD x the contiguous logical
         // range starting at x*(total/8) + min(x, total%8) (a bijection for any
@@ -352,6 +446,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         fb = logical / gx;
         tile = logical % gx;
     }
+    if (tile < 0) return;  // no item for this workgroup (uniform)
 
     const int n_tiles = a.tile_off[a.n_local];
     if (tile >= n_tiles) return;  // workgroup-uniform
