@@ -259,9 +259,12 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype, H, I))] int32, zeroed by the
  *             caller (rdg_fill_i32) before this call: after the down GEMM
  *             has stored a row tile's outputs for a block of columns it adds
- *             the block's column count to that tile's counter with release
- *             ordering at device scope; a tile is complete when its counter
- *             reaches rdg_signal_threshold(H, dtype) = H.
+ *             the block's column count to that tile's counter at device
+ *             scope, once those outputs are visible at device scope (they are
+ *             written through to memory and waited for: release ordering for
+ *             a reader that loads them at device scope, as rdg_combine does);
+ *             a tile is complete when its counter reaches
+ *             rdg_signal_threshold(H, dtype) = H.
  * Rows outside [offsets[e], offsets[e] + masked_m[e]) are neither read nor
  * written.  H and I must be multiples of 128.  A layout with L->n_rows = 0
  * is a no-op (nothing is launched; the buffer pointers may be NULL). */

@@ -12,8 +12,11 @@
 //
 // Design for CDNA4: one wave per (token, 512-feature slice); each lane owns
 // 8 consecutive features (a 16-byte bf16 vector), gathers the K expert rows
-// for them, accumulates in fp32 and writes once.  Slicing the row keeps a
-// 128-token decode batch from occupying only a handful of CUs.
+// for them (eight requests in flight, streamed past the caches: each row is
+// read once), accumulates in fp32 in slot order and writes once.  Slicing
+// the row keeps a 128-token decode batch from occupying only a handful of
+// CUs.  (Requesting the rows one slot at a time took 115 us on the 4096-token
+// prefill layer against 96 us, and 12.1 against 9.3 us on the decode layer.)
 //
 // The polling form (k_combine_poll) runs beside the signalled down GEMM on at
 // most a quarter of the CUs.  Each wave takes single layout rows, strided over
@@ -63,10 +66,10 @@ __device__ __forceinline__ void store8(void* o, size_t row, int H, int v, const 
 }
 
 // Lane 0 waits for a counter; returns false on timeout.  The polls are
-// relaxed device-scope loads: they read past this CU's L1 and any stale line
-// of this XCD's L2, where the producer's release (a write-back of its own L2)
-// is seen, without invalidating anything the GEMM waves sharing the CU rely
-// on.  Exponential back-off (64 cycles up to about 8k) keeps the polling
+// relaxed device-scope loads: they read memory, past this CU's L1 and any
+// stale line of this XCD's L2, where the producer's add lands after its
+// write-through row stores, without invalidating anything the GEMM waves
+// sharing the CU rely on.  Exponential back-off (64 cycles up to about 8k) keeps the polling
 // traffic on the counters' few cache lines low.
 __device__ bool wait_counter(const int32_t* c, int threshold, uint64_t timeout_ticks) {
     if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= threshold) return true;
@@ -103,6 +106,8 @@ __device__ __forceinline__ void token_slots(const int32_t* __restrict__ pos, con
 }
 
 // One 512-feature slice of token t: lane l owns features [8v, 8v+8), v = 64*slice + l.
+// The slots' rows are requested eight at a time (streamed: each is read
+// once), then summed in slot order.
 template <int YDT, int ODT>
 __device__ __forceinline__ void combine_slice(const void* __restrict__ y, const void* __restrict__ shared_out,
                                               void* __restrict__ out, int t, int slice, int K, int H,
@@ -110,14 +115,43 @@ __device__ __forceinline__ void combine_slice(const void* __restrict__ y, const 
     const int v = slice * kWave + lane;
     if (v >= H / 8) return;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-        const int pk = pos_l[k];
-        const float wk = w_l[k];
-        if (pk < 0) continue;
-        float yv[8];
-        load8<YDT>(y, (size_t)pk, H, v, yv);
+    constexpr int G = 8;
+    constexpr int NQ = YDT == RDG_BF16 ? 1 : 2;  // 16-byte pieces per lane and row
+    for (int k0 = 0; k0 < K; k0 += G) {
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        u32x4 q[G][NQ];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wk * yv[i];
+        for (int j = 0; j < G; ++j) {
+            const int k = k0 + j;
+            if (k < K && pos_l[k] >= 0) {
+                const u32x4* p = YDT == RDG_BF16
+                                     ? reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(y) +
+                                                                      (size_t)pos_l[k] * H) + v
+                                     : reinterpret_cast<const u32x4*>(static_cast<const float*>(y) +
+                                                                      (size_t)pos_l[k] * H) + 2 * v;
+#pragma unroll
+                for (int i = 0; i < NQ; ++i) q[j][i] = __builtin_nontemporal_load(p + i);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < G; ++j) {
+            const int k = k0 + j;
+            if (k >= K || pos_l[k] < 0) continue;
+            const float wk = w_l[k];
+            if (YDT == RDG_BF16) {
+                const uint32_t wd[4] = {q[j][0][0], q[j][0][1], q[j][0][2], q[j][0][3]};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc[2 * i] += wk * bf16_to_f32(wd[i] & 0xffffu);
+                    acc[2 * i + 1] += wk * bf16_to_f32(wd[i] >> 16);
+                }
+            } else {
+                const uint32_t wd[8] = {q[j][0][0], q[j][0][1], q[j][0][2], q[j][0][3],
+                                        q[j][NQ - 1][0], q[j][NQ - 1][1], q[j][NQ - 1][2], q[j][NQ - 1][3]};
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] += wk * __uint_as_float(wd[i]);
+            }
+        }
     }
     if (shared_out != nullptr) {
         float sv[8];
