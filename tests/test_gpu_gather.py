@@ -140,3 +140,40 @@ def test_gather_decode_workload_vs_oracle():
 def test_gather_prefill_workload_vs_oracle():
     cfg = dict(synth.WORKLOADS["prefill_bf16"])
     _full_layer(cfg, cfg["B"], 0, n_sample=256, seed=5, gather=True)
+
+
+# busy experts (several 128-row tiles) beside one-tile experts and empty
+# ones, so that the bf16 down GEMM runs its split work order (a one-tile
+# expert's panels back to back on one XCD, interleaved with the busy
+# experts' panel-major items), and a tiny layer where that order does not
+# fit the grid and the plain order runs; every token against the oracle,
+# both payload forms
+@pytest.mark.parametrize("counts", [[700, 40, 0, 300, 17, 129, 0, 64, 1, 128, 520, 33, 5, 0, 90, 256],
+                                    [100, 60]])
+@pytest.mark.parametrize("gather", [False, True])
+def test_tiled_busy_and_one_tile_experts(counts, gather):
+    import oracle
+    from harness import check_rows, out_as_f64, tolerance
+    from test_gpu_layer import _oracle_experts
+    m = rdg()
+    N = len(counts)
+    cfg = _small_cfg("bf16", N=N, n_group=1, topk_group=1, K=1, H=1024, I=512, wid=1500 + N)
+    B = int(sum(counts))
+    rng = np.random.default_rng(N)
+    ids_np = np.repeat(np.arange(N, dtype=np.int32), counts)[rng.permutation(B)].reshape(B, 1)
+    w_np = np.ones((B, 1), np.float32)
+    ids = torch.from_numpy(ids_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    x = synth.x(cfg, B, device=DEV)
+    experts = ExpertSet(cfg, range(N))
+    r = run_routed(cfg, x, None, ids, w, experts, 0, gather=gather)
+    torch.cuda.synchronize()
+    assert m.rdg_check_status(r["L"]) == (0, 0)
+    assert m.rdg_signal_rows(r["L"], m.RDG_BF16, cfg["H"], cfg["I"]) == 128  # the 128-row kernels
+    used = set(np.unique(ids_np).tolist())
+    ref = oracle.moe_layer(oracle.BF16, np_of(x), ids_np, w_np, _oracle_experts(experts, used))
+    got = np_of(r["out"])
+    err = oracle.rel_err(out_as_f64(got), out_as_f64(ref))
+    row = check_rows(got, ref, cfg, "busy and one-tile experts")
+    print("counts %s gather=%s rel_err=%.3e worst_row=%.3e" % (counts, gather, err, row), flush=True)
+    assert err <= tolerance(cfg), err
