@@ -60,8 +60,9 @@ def parse():
                    help="also measure every other workload and report it under 'workloads' (auto: with the "
                         "default workload and no variant flags)")
     p.add_argument("--extras", choices=["on", "off"], default="on",
-                   help="the measurements after the timed steps: heavy_experts (prefill layers) and the sbo "
-                        "comparison (prefill rank share); off for a kernel trace of the timed steps alone")
+                   help="the measurements after the timed steps: heavy_experts (prefill layers), the two "
+                        "dispatch forms on their own, and the sbo comparison (prefill rank share); off for a "
+                        "kernel trace of the timed steps alone")
     p.add_argument("--payload", choices=["gather", "copy"], default="gather",
                    help="dispatch payload: gather (the dispatch builds the layout only and the gate/up GEMM reads "
                         "each row's token through row_src) or copy (rows permuted into x_perm by the dispatch)")
@@ -679,6 +680,39 @@ def sbo_compare(b, steps, rounds=4):
             "overlap_pays": seq > sig, "rounds": rounds, "steps_per_round": per}
 
 
+def dispatch_forms(b, reps=20):
+    """The dispatch of this batch on its own (nothing running beside it), in
+    both payload forms: the layout only (ranks, scan, positions; the GEMM
+    then gathers the rows) and the layout plus the rows copied into x_perm.
+    The copy's algorithmic bytes: every token read once, every routed row
+    written once (+ fp8 scales)."""
+    torch, rdg, cfg = b.torch, b.rdg, b.cfg
+    H, K = cfg["H"], cfg["K"]
+    esz = {"f32": 4, "bf16": 2, "fp8": 1}[cfg["dtype"]]
+    ids = b.local if b.rank else b.ids
+    L = rdg.Layout(b.L.kind, b.L.n_local, b.T, K, b.dev, block_m=b.L.block_m, m_max=b.L.m_max)
+    xp = torch.empty((L.m_cap, H), dtype=b.sdt, device=b.dev)
+    xps = torch.empty((L.m_cap, H // 128), dtype=torch.float32, device=b.dev) if b.fp8 else None
+    x_s = b.x_s if b.fp8 else None
+    out = {}
+    for name, args in (("layout_only", (None, None)), ("with_copy", (xp, xps))):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        rdg.rdg_dispatch(b.x, x_s if args[0] is not None else None, b.DT, ids, L, *args)
+        ev[0].record()
+        for i in range(reps):
+            rdg.rdg_dispatch(b.x, x_s if args[0] is not None else None, b.DT, ids, L, *args)
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        out[name + "_us"] = round(1000 * ev[0].elapsed_time(ev[reps]) / reps, 2)
+    rows = int(b.L.masked_m.sum().item())
+    copy_bytes = b.T * H * esz + rows * H * esz + ((b.T + rows) * (H // 128) * 4 if b.fp8 else 0)
+    extra_us = out["with_copy_us"] - out["layout_only_us"]
+    out.update(copy_bytes=copy_bytes, copy_GBps=round(copy_bytes / (out["with_copy_us"] * 1e-6) / 1e9, 1),
+               copy_frac_of_hbm=round(copy_bytes / (out["with_copy_us"] * 1e-6) / 1e9 / HBM_PEAK_GBPS, 3),
+               copy_extra_us=round(extra_us, 2))
+    return out
+
+
 def heavy_experts(b, min_rows=315, reps=5):
     """The routed GEMMs restricted to the experts with at least `min_rows`
     rows (the rows per expert from which a bf16 tile's arithmetic outweighs
@@ -749,6 +783,8 @@ def main():
         line["sbo"]["polling_workgroups"] = b.poll_blocks
     if not b.rank and b.cfg["layout"] == "contiguous" and b.cfg["H"] >= 1024 and not args.tbo and args.extras == "on":
         line["heavy_experts"] = heavy_experts(b)
+    if not args.tbo and args.extras == "on":
+        line["dispatch"] = dispatch_forms(b)
     n_cpu = CPU_TOKENS[args.workload] if args.cpu_tokens is None else args.cpu_tokens
     if n_cpu != 0:
         line["cpu_baseline"] = cpu_baseline(b, n_cpu)
