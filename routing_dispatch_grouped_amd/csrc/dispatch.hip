@@ -104,11 +104,13 @@ __global__ __launch_bounds__(256) void k_rank(const int32_t* __restrict__ ids, i
     for (int e = lane; e < n_local; e += kWave) chunk_counts[(size_t)c * n_local + e] = cnt[e];
 }
 
-// Pass 2 runs as one workgroup of 256 threads (four waves, one per SIMD):
-// small enough in registers (about 60 per lane) to start beside a
-// workgroup of the 128-row GEMM, which leaves 96 of each SIMD's 512
-// registers free, so that a GEMM running on another stream (the shared
-// expert) does not hold up the dispatch.
+// Pass 2 runs as one workgroup of 256 threads (four waves, one per SIMD,
+// about 60 registers per lane), so that it can start on a CU where another
+// stream's GEMM workgroup (the shared expert's) leaves room beside it; a
+// 1024-thread form (four waves per SIMD) needed a whole CU to itself.  (The
+// 128-row bf16 GEMM's two waves per SIMD take 480 of the SIMD's 512
+// registers, so next to that one it still waits; its own work is 10-16 us
+// on a 4096-token batch.)
 constexpr int kScanThreads = 256;
 constexpr int kScanEPT = 4;  // experts per thread (n_local <= 1024)
 static_assert(kScanThreads * kScanEPT >= 1024 && kScanEPT == 4, "the 16-byte loads of k_scan hold four experts");
