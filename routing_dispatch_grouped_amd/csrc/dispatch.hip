@@ -294,7 +294,9 @@ __global__ __launch_bounds__(kScanThreads) void k_scan(int32_t* __restrict__ chu
 
 // Pass 3.  One wave per (token, 64-vector slice of its row): the slice-0
 // wave also publishes pos and row_src.  Without x_perm (a grouped GEMM that
-// gathers its token rows through row_src) only that wave runs per token.  row_bytes: bytes of one x row (a
+// gathers its token rows through row_src) only that wave runs per token.
+// chunk_base = NULL: pos was published by k_dispatch_small; only the rows
+// are copied.  row_bytes: bytes of one x row (a
 // multiple of 16); n_slices = ceil(row_bytes / 1024).
 __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, const float* __restrict__ x_s,
                                                  int row_bytes, int n_scales, int n_slices, int T, int K,
@@ -313,14 +315,18 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
     int p = -1;
     if (lane < K) {
         const int64_t i = (int64_t)t * K + lane;
-        const int e = ids[i];
-        if (e >= 0 && e < n_local) {
-            const int r = chunk_base[(size_t)(i / chunk) * n_local + e] + tmp_rank[i];
-            if (r < masked_m[e]) p = offsets[e] + r;
-        }
-        if (slice == 0) {
-            pos[i] = p;
-            if (p >= 0) row_src[p] = (int32_t)i;
+        if (chunk_base == nullptr) {
+            p = pos[i];  // published already (small dispatches): the copy only
+        } else {
+            const int e = ids[i];
+            if (e >= 0 && e < n_local) {
+                const int r = chunk_base[(size_t)(i / chunk) * n_local + e] + tmp_rank[i];
+                if (r < masked_m[e]) p = offsets[e] + r;
+            }
+            if (slice == 0) {
+                pos[i] = p;
+                if (p >= 0) row_src[p] = (int32_t)i;
+            }
         }
         dst_lds[wv][lane] = p;
     }
@@ -351,6 +357,168 @@ __global__ __launch_bounds__(256) void k_scatter(const uint8_t* __restrict__ x, 
                 if (pk >= 0) x_perm_s[(size_t)pk * n_scales + j] = sv;
             }
         }
+    }
+}
+
+// Small dispatches (at most kSmallEntries entries over at most kSmallExperts
+// experts: the decode batches and the decode rank share) in one workgroup of
+// 16 waves: the three passes above with the per-chunk counters in LDS
+// instead of memory and one launch instead of three.  Wave w ranks the
+// entries [w*chunk, (w+1)*chunk) as pass 1 does, the waves' counts are
+// scanned per expert in wave order (the chunk scan of pass 2), then the
+// experts' segments, and every wave publishes its entries' positions.
+// Padding rows are marked first; the workgroup barriers order those stores
+// before the positions' own.
+constexpr int kSmallWaves = 16;
+constexpr int kSmallSteps = 8;  // 64-entry steps per wave
+constexpr int kSmallEntries = kSmallWaves * kSmallSteps * kWave;  // 8192
+constexpr int kSmallExperts = 512;
+
+// Exclusive scan over a 1024-thread workgroup (16 waves); lds: 32 ints.
+__device__ int block_scan1024(int v, int* lds, int* total) {
+    const int lane = lane_id(), wv = threadIdx.x / kWave;
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const int y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    if (lane == kWave - 1) lds[wv] = x;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kSmallWaves; ++w) {
+        const int t = lds[w];
+        before += w < wv ? t : 0;
+        tot += t;
+    }
+    __syncthreads();
+    *total = tot;
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restrict__ ids, int n, int n_local,
+                                                         int nbits, int kind, int block_m, int m_max, int m_cap,
+                                                         int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                                                         int32_t* __restrict__ masked_m, int32_t* __restrict__ pos,
+                                                         int32_t* __restrict__ row_src,
+                                                         int32_t* __restrict__ tile_off, int32_t* __restrict__ status,
+                                                         int64_t* __restrict__ expert_load) {
+    __shared__ int cnt[kSmallWaves][kSmallExperts];  // per-wave counts, then each wave's base
+    __shared__ int s_off[kSmallExperts], s_keep[kSmallExperts];
+    __shared__ int lds[32];
+    const int wv = threadIdx.x / kWave, lane = lane_id();
+    if (threadIdx.x == 0 && status) {
+        status[0] = 0;
+        status[1] = 0;
+    }
+    for (int i = threadIdx.x; i < m_cap; i += blockDim.x) row_src[i] = -1;
+    for (int e = lane; e < n_local; e += kWave) cnt[wv][e] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+    // pass 1: stable ranks inside each wave's chunk
+    const int chunk = (n + kSmallWaves * kWave - 1) / (kSmallWaves * kWave) * kWave;  // <= kSmallSteps * 64
+    const uint64_t lt_mask = (1ull << lane) - 1ull;
+    int my_e[kSmallSteps], my_r[kSmallSteps];
+#pragma unroll
+    for (int p = 0; p < kSmallSteps; ++p) {
+        my_e[p] = -1;
+        my_r[p] = 0;
+        if (p * kWave >= chunk) continue;  // uniform
+        const int i = wv * chunk + p * kWave + lane;
+        int e = -1;
+        if (i < n) {
+            e = ids[i];
+            if (e < 0 || e >= n_local) e = -1;
+        }
+        const uint32_t key = (uint32_t)(e + 1);
+        uint64_t same = ~0ull;
+        for (int b = 0; b < nbits; ++b) {
+            const uint32_t bit = (key >> b) & 1u;
+            const uint64_t bal = __ballot(bit);
+            same &= bit ? bal : ~bal;
+        }
+        if (e >= 0) {
+            const int base = cnt[wv][e];
+            my_r[p] = base + __popcll(same & lt_mask);
+            if (lane == 63 - __clzll(same)) cnt[wv][e] = base + __popcll(same);
+        }
+        my_e[p] = e;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+    __syncthreads();
+
+    // pass 2: expert e's count and each wave's base (thread e), the segments
+    const int e = threadIdx.x;
+    const bool act = e < n_local;
+    int run = 0;
+    if (act) {
+#pragma unroll
+        for (int w = 0; w < kSmallWaves; ++w) {
+            const int v = cnt[w][e];
+            cnt[w][e] = run;
+            run += v;
+        }
+        counts[e] = run;
+        if (expert_load != nullptr)
+            atomicAdd(reinterpret_cast<unsigned long long*>(expert_load + e), (unsigned long long)run);
+    }
+    const int seg = !act ? 0 : kind == RDG_MASKED ? m_max : (run + block_m - 1) / block_m * block_m;
+    int total;
+    const int off = block_scan1024(seg, lds, &total);
+    int keep = run;
+    if (kind == RDG_MASKED && keep > m_max) keep = m_max;
+    if (kind == RDG_CONTIGUOUS) {
+        int room = m_cap - off;
+        if (room < 0) room = 0;
+        if (keep > room) keep = room;
+    }
+    if (!act) keep = 0;
+    if (act) {
+        offsets[e] = off;
+        masked_m[e] = keep;
+        s_off[e] = off;
+        s_keep[e] = keep;
+    }
+    if (e == 0) offsets[n_local] = total;
+    int worst = act ? run : 0;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) worst = max(worst, __shfl_xor(worst, o));
+    if (lane == 0) lds[16 + wv] = worst;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int m = 0;
+        for (int w = 0; w < kSmallWaves; ++w) m = max(m, lds[16 + w]);
+        if (kind == RDG_MASKED && m > m_max) set_status(status, RDG_ECAPACITY, m);
+        if (kind == RDG_CONTIGUOUS && total > m_cap) set_status(status, RDG_ECAPACITY, total);
+    }
+    for (int b = 0; b < kNumBT; ++b) {
+        const int nt = (keep + kBT[b] - 1) / kBT[b];
+        int tt;
+        const int to = block_scan1024(nt, lds, &tt);
+        if (act) tile_off[b * (n_local + 1) + e] = to;
+        if (e == 0) tile_off[b * (n_local + 1) + n_local] = tt;
+    }
+    __syncthreads();
+
+    // pass 3: positions
+#pragma unroll
+    for (int p = 0; p < kSmallSteps; ++p) {
+        if (p * kWave >= chunk) continue;  // uniform
+        const int i = wv * chunk + p * kWave + lane;
+        if (i >= n) continue;
+        int P = -1;
+        const int ee = my_e[p];
+        if (ee >= 0) {
+            const int r = cnt[wv][ee] + my_r[p];
+            if (r < s_keep[ee]) P = s_off[ee] + r;
+        }
+        pos[i] = P;
+        if (P >= 0) row_src[P] = i;
     }
 }
 
@@ -405,6 +573,21 @@ static hipError_t dispatch_passes(const void* x, const float* x_scales, int row_
     const int n_chunks = n > 0 ? (int)((n + chunk - 1) / chunk) : 0;
     int nbits = 1;
     while ((1 << nbits) < L.n_local + 1) ++nbits;
+    const int n_scales = x_scales && x_perm ? H / 128 : 0;
+
+    if (n <= kSmallEntries && L.n_local <= kSmallExperts) {
+        k_dispatch_small<<<1, kSmallWaves * kWave, 0, s>>>(ids, (int)n, L.n_local, nbits, L.kind, L.block_m, L.m_max,
+                                                           L.m_cap, L.counts, L.offsets, L.masked_m, L.pos,
+                                                           L.row_src, tile_off, L.status, L.expert_load);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess || T == 0 || x_perm == nullptr) return err;
+        const int n_slices = (row_bytes + 16 * kWave - 1) / (16 * kWave);
+        const int64_t units = (int64_t)T * n_slices;
+        k_scatter<<<(unsigned)((units + 3) / 4), 256, 0, s>>>(
+            static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales, n_slices, T, K, ids, L.n_local, chunk,
+            nullptr, nullptr, L.offsets, L.masked_m, L.pos, L.row_src, static_cast<uint8_t*>(x_perm), x_perm_scales);
+        return hipGetLastError();
+    }
 
     // pass 1 (also clears status and marks rows as padding)
     int blocks1 = (n_chunks + 3) / 4;
@@ -421,7 +604,6 @@ static hipError_t dispatch_passes(const void* x, const float* x_scales, int row_
     err = hipGetLastError();
     if (err != hipSuccess || T == 0) return err;
     // without x_perm only pos and row_src are published: one wave per token
-    const int n_scales = x_scales && x_perm ? H / 128 : 0;
     const int n_slices = x_perm ? (row_bytes + 16 * kWave - 1) / (16 * kWave) : 1;
     const int64_t units = (int64_t)T * n_slices;
     k_scatter<<<(unsigned)((units + 3) / 4), 256, 0, s>>>(static_cast<const uint8_t*>(x), x_scales, row_bytes, n_scales,
