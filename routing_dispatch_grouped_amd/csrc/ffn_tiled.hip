@@ -103,10 +103,17 @@ struct TOp<RDG_BF16> {
                 else w[s][rt] = *p;
             }
     }
-    // token operand of step s for local row r, lane group g: 16-byte piece 4s+g
+    // token operand of step s for the lane's row l = lane % 16 of a 16-row
+    // token tile, lane group g: 16-byte piece 4s+g.  The swizzle depends on
+    // l only, so the lane's offset is fixed per step and the token tile and
+    // ring slot add a constant (the LDS instruction's immediate offset).
+    static constexpr int XH = 1;  // 16-byte pieces per lane and step
     template <int CB>
-    __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
-        return *reinterpret_cast<const bf16x8_t*>(buf + r * CB + (piece_slot<CB>(r, s * 4 + g) << 4));
+    __device__ static int x_off(int l, int s, int g, int h) {
+        return l * CB + (piece_slot<CB>(l, s * 4 + g) << 4);
+    }
+    __device__ static op_t load_x(const uint8_t* p, const int (&xo)[XH]) {
+        return *reinterpret_cast<const bf16x8_t*>(p + xo[0]);
     }
     __device__ static f32x4_t mma(f32x4_t c, op_t a, op_t b) {
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -132,12 +139,15 @@ struct TOp<RDG_FP8_E4M3> {
                 w[s][rt] = r;
             }
     }
-    // 32 bytes: pieces 8s+2g and 8s+2g+1
+    // 32 bytes: pieces 8s+2g and 8s+2g+1 (lane offsets as for bf16)
+    static constexpr int XH = 2;
     template <int CB>
-    __device__ static op_t load_x(const uint8_t* buf, int r, int s, int g) {
-        const int c = s * 8 + g * 2;
-        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (piece_slot<CB>(r, c) << 4));
-        const i32x4_t b = *reinterpret_cast<const i32x4_t*>(buf + r * CB + (piece_slot<CB>(r, c + 1) << 4));
+    __device__ static int x_off(int l, int s, int g, int h) {
+        return l * CB + (piece_slot<CB>(l, s * 8 + g * 2 + h) << 4);
+    }
+    __device__ static op_t load_x(const uint8_t* p, const int (&xo)[XH]) {
+        const i32x4_t a = *reinterpret_cast<const i32x4_t*>(p + xo[0]);
+        const i32x4_t b = *reinterpret_cast<const i32x4_t*>(p + xo[1]);
         op_t o;
         o[0] = a[0]; o[1] = a[1]; o[2] = a[2]; o[3] = a[3];
         o[4] = b[0]; o[5] = b[1]; o[6] = b[2]; o[7] = b[3];
@@ -426,6 +436,12 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     const Ring ring[3] = {{lx0, ls0, lw0}, {lx1, ls1, lw1}, {lx2, ls0, lw0}};
 
     int fb, tile;
+    // The signalled form claims all 256 registers of its waves (two per SIMD
+    // fill the register file), so that the polling combine running beside
+    // it cannot put a wave on one of its SIMDs: with about 200 registers the
+    // pollers' spinning waves shared its SIMDs and the fp8 rank-share step
+    // took 1.87 ms instead of 1.80.
+    if constexpr (SIGNAL) asm volatile("" ::: "v255");
     if (SIGNAL) {
         // tile-major in dispatch order (grid x = column panel, padded to a
         // multiple of 8): row tiles complete in layout order for the polling
@@ -510,6 +526,13 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
                 dma4(src, rg.w + wv * 2 * S);
         }
     };
+    // the lane's LDS offsets of its token operand pieces, per step
+    int xo[S][O::XH];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+#pragma unroll
+        for (int h = 0; h < O::XH; ++h) xo[s][h] = O::template x_off<CB>(lane & 15, s, lane >> 4, h);
+
     // One chunk over the first NV 16-row token tiles: items i = (step s,
     // token tile ct) in order.  The token operand of item i+2 is read from
     // LDS while item i's MFMAs run (a three-deep register ring), and fp8
@@ -541,9 +564,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
         f32x4_t p[2][NRT];
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
         auto fetch = [&](int i) {
-            const int si = i / NV, r = (i % NV) * 16 + (lane & 15);
-            xb[i % 3] = O::template load_x<CB>(rg.x, r, si, lane >> 4);
-            if (FP8) sx[i % 4] = rg.s[r * SPB + si];
+            const int si = i / NV, ct = i % NV;
+            xb[i % 3] = O::load_x(rg.x + ct * 16 * CB, xo[si]);
+            if (FP8) sx[i % 4] = rg.s[(ct * 16 + (lane & 15)) * SPB + si];
         };
         auto promote = [&](int i) {  // fp8: item i's block partials into the accumulators
             const int si = i / NV, ct = i % NV;
