@@ -202,3 +202,29 @@ def test_expert_load_recorder():
         want += ref["counts"]
         assert np.array_equal(np_of(load), want)
     assert want.sum() > 0
+
+
+# batches of at most 8192 entries over at most 512 experts take the
+# one-workgroup dispatch, larger ones the three-pass form: both sides of
+# each limit, in both layouts (capacity drops included), with the payload
+# copied and the expert loads recorded
+@pytest.mark.parametrize("T,K,E,kind,m_max,holes", [
+    (1024, 8, 512, 0, 0, 0.0), (1025, 8, 512, 0, 0, 0.0), (1024, 8, 513, 0, 0, 0.0),
+    (1024, 8, 512, 1, 9, 0.0), (1025, 8, 512, 1, 9, 0.0), (1024, 8, 513, 1, 9, 0.0),
+    (1023, 8, 500, 0, 0, 0.3), (8192, 1, 3, 1, 4000, 0.0), (8193, 1, 3, 1, 4000, 0.0)])
+def test_small_and_large_dispatch_limits(T, K, E, kind, m_max, holes):
+    print("dispatch limits", T, K, E, kind, m_max, flush=True)
+    m = rdg()
+    ids = _ids(np.random.default_rng([T, K, E, kind]), T, K, E, skew=True, holes=holes)
+    load = torch.zeros(E, dtype=torch.int64, device=DEV)
+    L = m.Layout(kind, E, T, K, DEV, block_m=128, m_max=m_max, expert_load=load)
+    x = torch.randn((T, 256), device=DEV).to(torch.bfloat16)
+    xp = torch.zeros((L.m_cap, 256), dtype=torch.bfloat16, device=DEV)
+    m.rdg_dispatch(x, None, m.RDG_BF16, torch.from_numpy(ids).to(DEV), L, xp)
+    ref = oracle.layout(ids, E, oracle.MASKED if kind else oracle.CONTIGUOUS, block_m=128, m_max=m_max)
+    assert m.rdg_check_status(L) == (ref["status"], ref["detail"])
+    check_layout(L, ref, ids.shape)
+    assert np.array_equal(np_of(load), ref["counts"])
+    rs = ref["row_src"]
+    filled = np.flatnonzero(rs >= 0)
+    assert np.array_equal(np_of(xp)[filled], np_of(x)[rs[filled] // K])
