@@ -373,6 +373,8 @@ constexpr int kSmallWaves = 16;
 constexpr int kSmallSteps = 8;  // 64-entry steps per wave
 constexpr int kSmallEntries = kSmallWaves * kSmallSteps * kWave;  // 8192
 constexpr int kSmallExperts = 512;
+static_assert(kSmallWaves * kWave >= kSmallExperts && kSmallWaves <= 16,
+              "one thread per expert; the scans' wave totals at lds[0..15], the maxima at lds[16..31]");
 
 // Exclusive scan over a 1024-thread workgroup (16 waves); lds: 32 ints.
 __device__ int block_scan1024(int v, int* lds, int* total) {
@@ -412,7 +414,16 @@ __global__ __launch_bounds__(1024) void k_dispatch_small(const int32_t* __restri
         status[0] = 0;
         status[1] = 0;
     }
-    for (int i = threadIdx.x; i < m_cap; i += blockDim.x) row_src[i] = -1;
+    // every row starts as padding (the decode layer's masked layout clears
+    // 256 KiB here: 16-byte stores where row_src is 16-byte aligned)
+    int i0 = 0;
+    if ((reinterpret_cast<uintptr_t>(row_src) & 15) == 0) {
+        i0 = m_cap & ~3;
+        typedef int i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 pad = {-1, -1, -1, -1};
+        for (int i = threadIdx.x * 4; i < i0; i += blockDim.x * 4) *reinterpret_cast<i32x4*>(row_src + i) = pad;
+    }
+    for (int i = i0 + threadIdx.x; i < m_cap; i += blockDim.x) row_src[i] = -1;
     for (int e = lane; e < n_local; e += kWave) cnt[wv][e] = 0;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
