@@ -46,6 +46,8 @@ ALL_WORKLOADS = ["tiny_fp32", "decode_bf16", "prefill_bf16", "prefill_bf16_balan
 # of oracle time on 16 host threads
 CPU_TOKENS = {"tiny_fp32": -1, "decode_bf16": -1, "prefill_bf16": 192, "prefill_bf16_balanced": 96,
               "decode_rank_fp8": 256, "prefill_rank_fp8": 256}
+# polling-combine workgroups of the signalled step (prefill rank share)
+POLL_BLOCKS = 8
 SUMMARY_CPU_TOKENS = {"tiny_fp32": -1, "decode_bf16": 32, "prefill_bf16_balanced": 0, "decode_rank_fp8": 64,
                       "prefill_rank_fp8": 64, "prefill_bf16": 48}
 
@@ -80,6 +82,8 @@ def parse():
     p.add_argument("--tbo", action="store_true",
                    help="prefill layers as two micro-batches cut at a sequence boundary, on two streams "
                         "(the roofline then covers micro-batch A's gate/up)")
+    p.add_argument("--poll-blocks", type=int, default=POLL_BLOCKS,
+                   help="polling-combine workgroups in the signalled step (prefill rank share)")
     p.add_argument("--cpu-tokens", type=int, default=None,
                    help="tokens in the CPU-oracle FFN sample (-1: the whole batch; 0: skip; default per workload)")
     p.add_argument("--calibrate-copy", action="store_true",
@@ -448,9 +452,13 @@ class Bench:
         if cfg.get("signals"):
             rows = rdg.rdg_signal_rows(self.L, self.DT, cfg["H"], cfg["I"])
             self.signal_rows = rows
-            self.signals = torch.zeros(((self.L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=self.dev)
+            # the row tiles' counters, then the combine's unit counter and first finishing unit
+            self.signals = torch.zeros(((self.L.m_cap + rows - 1) // rows + 2,), dtype=torch.int32, device=self.dev)
             self.threshold = rdg.rdg_signal_threshold(cfg["H"], self.DT)
-            self.poll_blocks = 64  # the polling combine's workgroups (the library caps them at a quarter of the CUs)
+            # the polling combine's workgroups: they take the tokens of the row
+            # tiles that complete while the down GEMM runs, and the finishing
+            # combine after the GEMM takes the rest
+            self.poll_blocks = POLL_BLOCKS
             self.side = torch.cuda.Stream()
             self.gate_done = torch.cuda.Event()
         if cfg.get("shared_I"):
@@ -530,15 +538,18 @@ class Bench:
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
             self.stream.wait_stream(self.side)
             return
-        # signalled down GEMM on this stream; on the side stream the shared
-        # expert (overlapping gate/up), then the polling combine, released once
-        # gate/up is done so that it overlaps the down GEMM
+        # signalled down GEMM on this stream, then the finishing combine; on
+        # the side stream the shared expert (overlapping gate/up), then the
+        # polling combine, released once gate/up is done so that it overlaps
+        # the down GEMM
         rdg.rdg_fill_i32(self.signals, 0)
         self.side.wait_stream(self.stream)
         self._gate_up(timed)
         self.gate_done.record(self.stream)
         rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y,
                              self.signals)
+        rdg.rdg_combine_finish(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
+                               self.signal_rows)
         with self.torch.cuda.stream(self.side):
             self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             self.side.wait_event(self.gate_done)
@@ -773,6 +784,8 @@ def main():
     side = cu_masked_stream(args.side_cus) if args.side_cus else None
     b = Bench(args.workload, dev, ue8m0=args.ue8m0, tbo=args.tbo, replicas=args.eplb_replicas, side_cus=args.side_cus,
               side_stream=side, payload=args.payload)
+    if getattr(b, "signals", None) is not None:
+        b.poll_blocks = args.poll_blocks
     res = measure(b, args, args.steps, args.warmup, args.workload)
     line = {"metric": res["metric"], "value": res["value"], "unit": res["unit"], "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": res["ms_per_step"], "higher_is_better": True, "scaling": "weak",

@@ -11,7 +11,8 @@
  *                    (rdg_grouped_ffn_gather: reading the token rows through
  *                    the layout instead of a permuted copy)
  *   rdg_combine      routing-weighted unpermute-and-sum (optionally polling
- *                    the down GEMM's per-row-tile completion signals)
+ *                    the down GEMM's per-row-tile completion signals;
+ *                    rdg_combine_finish: the rest once the GEMM is done)
  *
  * Page names used in the citations below:
  *   [LEP]  "Large-scale EP: DeepEP, EPLB and two-batch overlap" (SGLang handbook)
@@ -256,8 +257,9 @@ int rdg_layout_dense(int T, const rdg_layout* L, rdg_stream_t stream);
  * per-block promotion.
  *   h_ws      [m_cap, I] (dtype's storage: fp32 / bf16 / e4m3)
  *   y         [m_cap, H] fp32 (RDG_F32) or bf16
- *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype, H, I))] int32, zeroed by the
- *             caller (rdg_fill_i32) before this call: after the down GEMM
+ *   signals   NULL, or [ceil(m_cap / rdg_signal_rows(L, dtype, H, I)) + 2] int32, zeroed by
+ *             the caller (rdg_fill_i32) before this call (the last two words
+ *             are the polling combine's, see rdg_combine): after the down GEMM
  *             has stored a row tile's outputs for a block of columns it adds
  *             the block's column count to that tile's counter at device
  *             scope, once those outputs are visible at device scope (they are
@@ -343,7 +345,9 @@ int rdg_signal_threshold(int H, int dtype);
  *              signal_rows = rdg_signal_rows(L, dtype, H, I) of that call,
  *              threshold and a timeout in microseconds (a tile still
  *              incomplete then is skipped and status = RDG_ETIMEOUT with
- *              detail = the tile index)
+ *              detail = the tile index).  Word ceil(m_cap / signal_rows) of
+ *              the array (zeroed with the counters) counts the work units
+ *              the polling waves have claimed
  *   max_blocks 0 = one wavefront per token and 512-feature slice; else at
  *              most this many 256-thread workgroups loop over the work.  The
  *              polling form never uses more than a quarter of the GPU's CUs'
@@ -353,11 +357,30 @@ int rdg_signal_threshold(int H, int dtype);
  * The polling form may run on another stream concurrently with the down
  * GEMM, which must have been enqueued first.  Each token is combined at its
  * last layout row (L->row_src must be set), once every row tile it reads is
- * complete, and the tokens with no local row after them.  The output does
- * not depend on the visiting order: it equals the plain form bit for bit. */
+ * complete, and the tokens with no local row after them; the waves claim
+ * these units in layout order, one at a time, until none are left or
+ * rdg_combine_finish has taken the rest.  The output does not depend on the
+ * visiting order: it equals the plain form bit for bit.  RDG_EUNSUPPORTED
+ * when m_cap + ceil(T / 64) reaches 2^30. */
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
-                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
+                const void* shared_out, void* out, int out_dtype, int32_t* signals, int signal_rows,
                 int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream);
+
+/* The rest of a polling combine ([SBO] section 2: the consumer takes each
+ * row block as its counter completes; once the producer has finished there
+ * is nothing left to wait for).  Enqueue it on the down GEMM's stream after
+ * rdg_grouped_ffn / rdg_grouped_down, while the polling rdg_combine with the
+ * same signals runs on another stream.  It closes the polling form's unit
+ * counter (polling waves stop claiming) and combines every token whose unit
+ * no polling wave had claimed, one wavefront per token and 512-feature slice
+ * as the plain form does; the polling waves finish the units they hold.
+ * Each token is combined exactly once, and out equals the plain form bit for
+ * bit.  The output is complete once both this call and the polling combine
+ * have finished.  Arguments as for rdg_combine (signals and signal_rows
+ * required). */
+int rdg_combine_finish(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
+                       const void* shared_out, void* out, int out_dtype, int32_t* signals, int signal_rows,
+                       rdg_stream_t stream);
 
 /* fp8 e4m3 block quantiser (the "1d2d" scales of [SBO] section 3): blocks of
  * block_rows x 128 (1 for activations, 128 for weights); scale = amax/448 in

@@ -57,6 +57,7 @@ _SIGS = {
     "rdg_signal_rows": ([_LP, _I, _I, _I], _I),
     "rdg_signal_threshold": ([_I, _I], _I),
     "rdg_combine": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _I, _I64, _I, _P], _I),
+    "rdg_combine_finish": ([_P, _I, _LP, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P], _I),
     "rdg_quantize_fp8": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "rdg_quantize_fp8_ue8m0": ([_P, _I, _I, _I, _I, _P, _P, _P], _I),
     "rdg_fill_i32": ([_P, ctypes.c_int32, _I64, _P], _I),
@@ -255,6 +256,13 @@ def rdg_combine(y, y_dtype, layout, topk_w, T, K, H, shared_out, out, out_dtype,
     _check(_lib.rdg_combine(_ptr(y), y_dtype, layout.ref, _ptr(topk_w), T, K, H, _ptr(shared_out), _ptr(out),
                             out_dtype, _ptr(signals), signal_rows, threshold, timeout_us, max_blocks,
                             _stream(stream)), "rdg_combine")
+
+
+def rdg_combine_finish(y, y_dtype, layout, topk_w, T, K, H, shared_out, out, out_dtype, signals, signal_rows,
+                       stream=None):
+    _check(_lib.rdg_combine_finish(_ptr(y), y_dtype, layout.ref, _ptr(topk_w), T, K, H, _ptr(shared_out),
+                                   _ptr(out), out_dtype, _ptr(signals), signal_rows, _stream(stream)),
+           "rdg_combine_finish")
 
 
 def rdg_quantize_fp8(src, src_dtype, block_rows, q, scales, stream=None):

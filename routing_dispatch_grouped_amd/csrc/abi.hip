@@ -289,7 +289,7 @@ int rdg_grouped_down(const rdg_layout* L, int dtype, int H, int I, const void* h
 }
 
 int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
-                const void* shared_out, void* out, int out_dtype, const int32_t* signals, int signal_rows,
+                const void* shared_out, void* out, int out_dtype, int32_t* signals, int signal_rows,
                 int threshold, int64_t timeout_us, int max_blocks, rdg_stream_t stream) {
     if (!layout_ok(L) || !L->pos || T < 0 || K < 1 || K > 32 || H < 8 || H % 8 != 0) return RDG_EINVAL;
     if ((int64_t)T * K != L->n_rows) return RDG_EINVAL;
@@ -304,11 +304,29 @@ int rdg_combine(const void* y, int y_dtype, const rdg_layout* L, const float* to
     if (signals) {
         if (threshold < 1 || timeout_us < 0 || !L->status || !L->row_src) return RDG_EINVAL;
         if (signal_rows != 16 && signal_rows != 32 && signal_rows != 64 && signal_rows != 128) return RDG_EINVAL;
+        if (L->m_cap + ((int64_t)T + 63) / 64 >= (1 << 30)) return RDG_EUNSUPPORTED;  // unit counter range
         rows_per_sig = signal_rows;
         ticks = (uint64_t)timeout_us * wall_ticks_per_us();
     }
     return hip_rc(launch_combine(y, y_dtype, L->pos, L->row_src, L->m_cap, topk_w, T, K, H, shared_out, out,
                                  out_dtype, signals, rows_per_sig, threshold, ticks, max_blocks, L->status, stream));
+}
+
+int rdg_combine_finish(const void* y, int y_dtype, const rdg_layout* L, const float* topk_w, int T, int K, int H,
+                       const void* shared_out, void* out, int out_dtype, int32_t* signals, int signal_rows,
+                       rdg_stream_t stream) {
+    if (!layout_ok(L) || !L->pos || T < 0 || K < 1 || K > 32 || H < 8 || H % 8 != 0) return RDG_EINVAL;
+    if ((int64_t)T * K != L->n_rows) return RDG_EINVAL;
+    if (!((y_dtype == RDG_BF16 && (out_dtype == RDG_BF16 || out_dtype == RDG_F32)) ||
+          (y_dtype == RDG_F32 && out_dtype == RDG_F32)))
+        return RDG_EUNSUPPORTED;
+    if (!signals) return RDG_EINVAL;
+    if (signal_rows != 16 && signal_rows != 32 && signal_rows != 64 && signal_rows != 128) return RDG_EINVAL;
+    if (L->m_cap + ((int64_t)T + 63) / 64 >= (1 << 30)) return RDG_EUNSUPPORTED;
+    if (T > 0 && (!y || !topk_w || !out || !aligned16(y) || !aligned16(out))) return RDG_EINVAL;
+    if (shared_out && !aligned16(shared_out)) return RDG_EINVAL;
+    return hip_rc(launch_combine_finish(y, y_dtype, L->pos, L->m_cap, topk_w, T, K, H, shared_out, out, out_dtype,
+                                        signals, signal_rows, stream));
 }
 
 int rdg_quantize_fp8(const void* src, int src_dtype, int rows, int cols, int block_rows, uint8_t* q,

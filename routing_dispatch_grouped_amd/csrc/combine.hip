@@ -19,13 +19,18 @@
 // prefill layer against 96 us, and 12.1 against 9.3 us on the decode layer.)
 //
 // The polling form (k_combine_poll) runs beside the signalled down GEMM on at
-// most a quarter of the CUs.  Each wave takes single layout rows, strided over
-// the whole layout, and combines every token whose last row it is, after lane
-// 0 has waited for the counter of each row tile the token reads; a bounded
-// wait turns a tile that never completes into a status code instead of a
-// hang.  The published rows are staged in LDS by device-scope direct loads,
-// many in flight per wave, so that a wave is not bound by one memory round
-// trip per 512-feature slice.
+// most a quarter of the CUs.  Each wave claims single layout rows in layout
+// order from a counter (the row tiles complete in that order) and combines
+// every token whose last row it is, after lane 0 has waited for the counter
+// of each row tile the token reads; a bounded wait turns a tile that never
+// completes into a status code instead of a hang.  The published rows are
+// staged in LDS by device-scope direct loads, many in flight per wave, so that
+// a wave is not bound by one memory round trip per 512-feature slice.  The
+// finishing form, enqueued after the down GEMM on its stream, closes the
+// counter and combines every token the polling waves had not claimed with
+// the plain form's parallelism (k_combine_close, then k_combine<.., true>):
+// a few polling workgroups take the tokens of the tiles that complete early,
+// and the rest no longer waits for them.
 #include "rdg_internal.h"
 
 namespace rdg {
@@ -163,22 +168,45 @@ __device__ __forceinline__ void combine_slice(const void* __restrict__ y, const 
 }
 
 // Plain form: one wave per (token, 512-feature slice) unit, tokens in index
-// order.
-template <int YDT, int ODT>
+// order.  FINISH: only the tokens whose polling unit (see k_combine_poll: the
+// token's last layout row, or m_cap + t / 64 without one) is at or past
+// *start, the first unit no polling wave claimed.
+template <int YDT, int ODT, bool FINISH>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y, const int32_t* __restrict__ pos,
                                                  const float* __restrict__ w, int T, int K, int H,
-                                                 const void* __restrict__ shared_out, void* __restrict__ out) {
+                                                 const void* __restrict__ shared_out, void* __restrict__ out,
+                                                 int m_cap, const int32_t* __restrict__ start) {
     __shared__ int pos_lds[4][32];
     __shared__ float w_lds[4][32];
     const int wv = threadIdx.x / kWave, lane = lane_id();
     const int n_slices = (H / 8 + kWave - 1) / kWave;
     const int64_t stride = (int64_t)gridDim.x * 4;
     const int64_t n_units = (int64_t)T * n_slices;
+    const int u0 = FINISH ? *start : 0;
     for (int64_t unit = (int64_t)blockIdx.x * 4 + wv; unit < n_units; unit += stride) {
         const int t = (int)(unit / n_slices), slice = (int)(unit % n_slices);
         token_slots(pos, w, t, K, pos_lds[wv], w_lds[wv], lane);
+        if constexpr (FINISH) {
+            int last = -1;
+            for (int k = 0; k < K; ++k) last = max(last, pos_lds[wv][k]);
+            const int64_t u = last >= 0 ? (int64_t)last : (int64_t)m_cap + t / kWave;
+            if (u < u0) continue;  // combined by a polling wave (uniform)
+        }
         combine_slice<YDT, ODT>(y, shared_out, out, t, slice, K, H, pos_lds[wv], w_lds[wv], lane);
     }
+}
+
+// Closes the polling form's unit counter: polling waves that claim after
+// this get a unit >= kClaimClosed and stop; every unit below the counter's
+// value before the close is theirs, every unit from it on the finishing
+// form's.
+constexpr int32_t kClaimClosed = 1 << 30;
+__global__ void k_combine_close(int32_t* claim, int32_t* start, int n_units) {
+    if (threadIdx.x != 0) return;
+    const int32_t old = __hip_atomic_fetch_add(claim, kClaimClosed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // closed before (old >= kClaimClosed, or wrapped negative by repeated
+    // closes): nothing is left for this call
+    *start = old >= 0 && old < n_units ? old : n_units;
 }
 
 // Eight features of a published row (device-scope loads: see load8_published),
@@ -236,10 +264,10 @@ __device__ __forceinline__ void dma16_device_scope(const void* src, const void* 
 
 // Polling form.  Units: one layout row each (a token is combined at its
 // last layout row, max_k pos[t,k]), then units of 64 tokens (the tokens with
-// no row here, which get the shared output or zero).  Wave g of the grid
-// takes units g, g + waves, g + 2 waves, ...: every wave's units are spread
-// over the layout, so when the down GEMM's last row tiles complete, their
-// tokens are combined by many waves at once.  Per token: lane k < K holds
+// no row here, which get the shared output or zero).  Each wave claims the
+// next unit from *claim (a relaxed device-scope add; the row tiles complete
+// in layout order, so the claimed units follow the down GEMM) until the
+// units run out or the finishing form has closed the counter.  Per token: lane k < K holds
 // slot k; lane 0 waits for the counter of each row tile the token reads (the
 // last confirmed tile is remembered).  Then the token's rows are staged in
 // groups: for bf16 rows, SB 512-feature pieces per wave go through LDS by
@@ -252,16 +280,19 @@ __global__ __launch_bounds__(256) void k_combine_poll(const void* __restrict__ y
                                                       const float* __restrict__ w, int T, int K, int H,
                                                       const void* __restrict__ shared_out, void* __restrict__ out,
                                                       const int32_t* signals, int rows_per_sig, int threshold,
-                                                      uint64_t timeout_ticks, int32_t* status) {
+                                                      uint64_t timeout_ticks, int32_t* claim, int32_t* status) {
     constexpr int SB = 8;  // staged pieces of 64 lanes x 16 bytes per wave
     __shared__ __attribute__((aligned(16))) uint8_t stage[4][SB][1024];
     const int lane = lane_id(), wv = threadIdx.x / kWave;
-    const int64_t waves = (int64_t)gridDim.x * (blockDim.x / kWave);
     const int64_t row_units = m_cap;
     const int64_t n_units = row_units + ((int64_t)T + kWave - 1) / kWave;
     const int nvec = H / 8, n_slices = (nvec + kWave - 1) / kWave;
     int known_tile = -1;
-    for (int64_t u = (int64_t)blockIdx.x * (blockDim.x / kWave) + wv; u < n_units; u += waves) {
+    for (;;) {
+        int claimed = 0;
+        if (lane == 0) claimed = __hip_atomic_fetch_add(claim, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int64_t u = __shfl(claimed, 0);
+        if (u < 0 || u >= n_units) break;  // uniform: no units left, or closed (wrapped if closed twice)
         int tok = -1;
         bool mine = false;
         if (u < row_units) {
@@ -399,10 +430,12 @@ __global__ __launch_bounds__(256) void k_combine_poll(const void* __restrict__ y
 
 hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int32_t* row_src, int m_cap,
                           const float* w, int T, int K, int H, const void* shared_out, void* out, int out_dt,
-                          const int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
+                          int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
                           int max_blocks, int32_t* status, hipStream_t s) {
     if (T == 0) return hipSuccess;
     const bool ready = signals != nullptr;
+    // the unit counter follows the row tiles' counters
+    int32_t* claim = ready ? signals + (m_cap + rows_per_sig - 1) / rows_per_sig : nullptr;
     int64_t blocks;
     if (ready) {
         // Polling workgroups hold their CU's resources while they wait, and a
@@ -431,15 +464,35 @@ hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int
         if (ready)                                                                                               \
             k_combine_poll<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, row_src, m_cap, w, T, K, H,           \
                                                                   shared_out, out, signals, rows_per_sig,       \
-                                                                  threshold, timeout_ticks, status);            \
+                                                                  threshold, timeout_ticks, claim, status);     \
         else                                                                                                     \
-            k_combine<YD, OD><<<(unsigned)blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out);             \
+            k_combine<YD, OD, false><<<(unsigned)blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, 0,     \
+                                                                     nullptr);                                  \
     } while (0)
     if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_COMBINE(RDG_BF16, RDG_BF16);
     else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_COMBINE(RDG_BF16, RDG_F32);
     else if (y_dt == RDG_F32 && out_dt == RDG_F32) RDG_COMBINE(RDG_F32, RDG_F32);
     else return hipErrorInvalidValue;
 #undef RDG_COMBINE
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_finish(const void* y, int y_dt, const int32_t* pos, int m_cap, const float* w, int T, int K,
+                                 int H, const void* shared_out, void* out, int out_dt, int32_t* signals,
+                                 int rows_per_sig, hipStream_t s) {
+    if (T == 0) return hipSuccess;
+    int32_t* claim = signals + (m_cap + rows_per_sig - 1) / rows_per_sig;
+    const int64_t n_units = (int64_t)m_cap + ((int64_t)T + kWave - 1) / kWave;
+    k_combine_close<<<1, kWave, 0, s>>>(claim, claim + 1, (int)n_units);
+    const int64_t units = (int64_t)T * ((H / 8 + kWave - 1) / kWave);
+    const unsigned blocks = (unsigned)((units + 3) / 4);
+#define RDG_FINISH(YD, OD) \
+    k_combine<YD, OD, true><<<blocks, 256, 0, s>>>(y, pos, w, T, K, H, shared_out, out, m_cap, claim + 1)
+    if (y_dt == RDG_BF16 && out_dt == RDG_BF16) RDG_FINISH(RDG_BF16, RDG_BF16);
+    else if (y_dt == RDG_BF16 && out_dt == RDG_F32) RDG_FINISH(RDG_BF16, RDG_F32);
+    else if (y_dt == RDG_F32 && out_dt == RDG_F32) RDG_FINISH(RDG_F32, RDG_F32);
+    else return hipErrorInvalidValue;
+#undef RDG_FINISH
     return hipGetLastError();
 }
 

@@ -217,7 +217,12 @@ bool tiled_supported(int dtype, int H, int I);                 // shapes the bt 
 
 hipError_t launch_combine(const void* y, int y_dt, const int32_t* pos, const int32_t* row_src, int m_cap,
                           const float* w, int T, int K, int H, const void* shared_out, void* out, int out_dt,
-                          const int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
+                          int32_t* signals, int rows_per_sig, int threshold, uint64_t timeout_ticks,
                           int max_blocks, int32_t* status, hipStream_t s);
+// signals: the row tiles' counters, then the polling form's unit counter and
+// the finishing form's first unit
+hipError_t launch_combine_finish(const void* y, int y_dt, const int32_t* pos, int m_cap, const float* w, int T, int K,
+                                 int H, const void* shared_out, void* out, int out_dt, int32_t* signals,
+                                 int rows_per_sig, hipStream_t s);
 
 }  // namespace rdg

@@ -117,11 +117,13 @@ def quantize_act(x, pow2=False):
 
 
 def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max=0, shared_out=None,
-               signals=False, max_blocks=0, concurrent=False, timeout_us=2_000_000, gather=False):
+               signals=False, max_blocks=0, concurrent=False, timeout_us=2_000_000, gather=False, finish=False):
     """dispatch -> grouped FFN -> combine on the device.  Returns a dict of
     device tensors (layout, x_perm, h, y, out).  gather: the dispatch builds
     the layout only and the grouped FFN reads the token rows through it
-    (rdg_grouped_ffn_gather; x_perm is then None)."""
+    (rdg_grouped_ffn_gather; x_perm is then None).  finish (with signals):
+    rdg_combine_finish after the down GEMM on its stream, beside the polling
+    combine."""
     m = rdg()
     dt = dt_code(cfg)
     T, H = x.shape
@@ -153,9 +155,11 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
     sig = None
     thr = 0
     rows = 0
+    n_sig = 0
     if signals:
         rows = m.rdg_signal_rows(L, dt, H, I)
-        sig = torch.empty(((L.m_cap + rows - 1) // rows,), dtype=torch.int32, device=x.device)
+        n_sig = (L.m_cap + rows - 1) // rows  # the row tiles' counters, then the combine's two words
+        sig = torch.empty((n_sig + 2,), dtype=torch.int32, device=x.device)
         m.rdg_fill_i32(sig, 0)
         thr = m.rdg_signal_threshold(H, dt)
     out_dt = m.RDG_F32 if dt == m.RDG_F32 else m.RDG_BF16
@@ -175,13 +179,17 @@ def run_routed(cfg, x, x_s, local_ids, topk_w, experts, kind, block_m=128, m_max
         with torch.cuda.stream(s_comb):
             m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0,
                           thr, timeout_us, max_blocks, stream=s_comb)
+        if finish:
+            m.rdg_combine_finish(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows, stream=s_gemm)
         s_gemm.wait_stream(s_comb)
     else:
         ffn()
         m.rdg_combine(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows if signals else 0, thr,
                       timeout_us, max_blocks)
+        if finish:
+            m.rdg_combine_finish(y, y_dt, L, topk_w, T, K, H, shared_out, out, out_dt, sig, rows)
     return dict(L=L, x_perm=x_perm, x_perm_s=x_perm_s, h=h, h_s=h_s, y=y, out=out, signals=sig, threshold=thr,
-                signal_rows=rows)
+                signal_rows=rows, n_sig=n_sig)
 
 
 def run_shared(cfg, x, x_s, shared):

@@ -287,7 +287,7 @@ def test_prefill_rank_fp8_workload_sbo():
     # every row tile's counter reached the threshold exactly; unused counters stayed 0
     L = r["L"]
     rows = r["signal_rows"]
-    sig = np_of(r["signals"])
+    sig = np_of(r["signals"])[:r["n_sig"]]
     off = np_of(L.offsets)
     mm = np_of(L.masked_m)
     want = np.zeros_like(sig)
@@ -296,15 +296,16 @@ def test_prefill_rank_fp8_workload_sbo():
             want[(off[e] + j * rows) // rows] = r["threshold"]
     assert np.array_equal(sig, want)
     # the signalled, concurrent run equals the plain sequential run bit for bit,
-    # on every repeat (the overlap must not change a single bit)
+    # on every repeat (the overlap must not change a single bit), with the
+    # polling combine alone and with the finishing form beside it
     r2 = run_routed(cfg, xq, x_s, loc, share["w_dev"], experts, m.RDG_CONTIGUOUS, block_m=128)
-    for rep in range(3):
+    for rep, finish, mb in ((0, False, 64), (1, True, 16), (2, True, 4)):
         r3 = run_routed(cfg, xq, x_s, loc, share["w_dev"], experts, m.RDG_CONTIGUOUS, block_m=128, signals=True,
-                        concurrent=True, max_blocks=64)
+                        concurrent=True, max_blocks=mb, finish=finish)
         assert m.rdg_check_status(r3["L"]) == (0, 0)
         ndiff = int((r3["out"] != r2["out"]).any(1).sum())
-        print("repeat %d of the signalled run: tokens differing from the sequential run: %d" % (rep, ndiff),
-              flush=True)
+        print("repeat %d of the signalled run (finish=%s, %d polling workgroups): tokens differing from the "
+              "sequential run: %d" % (rep, finish, mb, ndiff), flush=True)
         assert ndiff == 0
         del r3
     vr = _valid_rows(r2["L"])
@@ -349,7 +350,8 @@ def test_prefill_rank_fp8_workload_sbo():
 @pytest.mark.parametrize("dtype", ["f32", "bf16", "fp8", "fp8u"])
 @pytest.mark.parametrize("B", [40, 300, 600])
 @pytest.mark.parametrize("kind", [0, 1])
-def test_sbo_small(dtype, B, kind):
+@pytest.mark.parametrize("finish", [False, True])
+def test_sbo_small(dtype, B, kind, finish):
     m = rdg()
     cfg = _small_cfg(dtype, wid=500 + B + kind)
     dt = dt_code(cfg)
@@ -367,10 +369,10 @@ def test_sbo_small(dtype, B, kind):
     m_max = ((B + 127) // 128) * 128 if kind == m.RDG_MASKED else 0
     seq = run_routed(cfg, x, x_s, loc, w, experts, kind, block_m=128, m_max=m_max)
     sbo = run_routed(cfg, x, x_s, loc, w, experts, kind, block_m=128, m_max=m_max, signals=True, concurrent=True,
-                     max_blocks=8)
+                     max_blocks=2 if finish else 8, finish=finish)
     assert m.rdg_check_status(sbo["L"]) == (0, 0)
     rows = sbo["signal_rows"]
-    sig, off, mm = np_of(sbo["signals"]), np_of(sbo["L"].offsets), np_of(sbo["L"].masked_m)
+    sig, off, mm = np_of(sbo["signals"])[:sbo["n_sig"]], np_of(sbo["L"].offsets), np_of(sbo["L"].masked_m)
     want = np.zeros_like(sig)
     for e in range(n_local):
         for j in range((mm[e] + rows - 1) // rows):
@@ -378,8 +380,8 @@ def test_sbo_small(dtype, B, kind):
     assert np.array_equal(sig, want)
     orphans = int((loc_np < 0).all(1).sum())
     ndiff = int((sbo["out"] != seq["out"]).any(1).sum())
-    print("sbo small %s B=%d kind=%d rows/signal=%d orphans=%d differing=%d" % (dtype, B, kind, rows, orphans, ndiff),
-          flush=True)
+    print("sbo small %s B=%d kind=%d finish=%s rows/signal=%d orphans=%d differing=%d"
+          % (dtype, B, kind, finish, rows, orphans, ndiff), flush=True)
     assert orphans > 0 and ndiff == 0
     used = set(np.unique(loc_np[loc_np >= 0]).tolist())
     ref = oracle.moe_layer(dt, xo, loc_np, rw, [experts.oracle_expert(j) if j in used else None
@@ -405,8 +407,9 @@ def test_sbo_timeout_is_reported_not_hung():
     r = run_routed(cfg, x, None, ids, w, experts, m.RDG_CONTIGUOUS, block_m=128, signals=True)
     assert m.rdg_check_status(r["L"]) == (0, 0)
     out = torch.empty_like(r["out"])
+    m.rdg_fill_i32(r["signals"][r["n_sig"]:], 0)  # the combine's unit counter starts again
     m.rdg_combine(r["y"], m.RDG_BF16, r["L"], w, B, cfg["K"], cfg["H"], None, out, m.RDG_BF16, r["signals"],
                   r["signal_rows"], r["threshold"] + 1, 2000, 4)
     code, detail = m.rdg_check_status(r["L"])
     assert code == m.RDG_ETIMEOUT
-    assert 0 <= detail < len(r["signals"])
+    assert 0 <= detail < r["n_sig"]
