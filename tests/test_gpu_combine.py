@@ -61,3 +61,67 @@ def test_combine_parity(T, K, E, H, ydt, shared):
         bound = np.maximum(np.abs(rd), np.abs(gd)) * 2.0 ** -7 + mag * (K + 2) * 2.0 ** -24 + 1e-30
         assert np.all(np.abs(gd - rd) <= bound)
         assert np.mean(g != ref) < 1e-3
+
+
+def test_finishing_form_alone_repeated_and_after_polling_stops():
+    """rdg_combine_finish with no polling combine beside it takes every token
+    (equal to the plain form bit for bit); a second call finds the counter
+    closed and combines nothing; a polling combine started after the close
+    claims nothing and waits for no tile (its counters are never signalled
+    here); zeroing the two words hands everything to the next call again."""
+    m = rdg()
+    T, K, E, H = 300, 6, 20, 1024
+    rng = np.random.default_rng(91)
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.2] = -1
+    ids[:7] = -1  # tokens without a row
+    w = torch.from_numpy(rng.random((T, K)).astype(np.float32)).to(DEV)
+    L = m.Layout(m.RDG_CONTIGUOUS, E, T, K, DEV, block_m=16)
+    dummy = torch.zeros((T, 16), dtype=torch.float32, device=DEV)
+    xp = torch.zeros((L.m_cap, 16), dtype=torch.float32, device=DEV)
+    m.rdg_dispatch(dummy, None, m.RDG_F32, torch.from_numpy(ids).to(DEV), L, xp)
+    y = torch.randn((L.m_cap, H), device=DEV).to(torch.bfloat16)
+    sh = torch.randn((T, H), device=DEV).to(torch.bfloat16)
+    ref = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    m.rdg_combine(y, m.RDG_BF16, L, w, T, K, H, sh, ref, m.RDG_BF16)
+    rows = 16
+    n_sig = (L.m_cap + rows - 1) // rows
+    sig = torch.zeros((n_sig + 2,), dtype=torch.int32, device=DEV)
+    out = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    m.rdg_combine_finish(y, m.RDG_BF16, L, w, T, K, H, sh, out, m.RDG_BF16, sig, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert int(sig[n_sig + 1]) == 0  # the first unit no polling wave held
+    poison = torch.full_like(out, float("nan"))
+    out.copy_(poison)
+    m.rdg_combine_finish(y, m.RDG_BF16, L, w, T, K, H, sh, out, m.RDG_BF16, sig, rows)
+    m.rdg_combine(y, m.RDG_BF16, L, w, T, K, H, sh, out, m.RDG_BF16, sig, rows, 1, 2_000_000, 4)
+    torch.cuda.synchronize()
+    assert m.rdg_check_status(L) == (0, 0)
+    assert torch.equal(out.view(torch.int16), poison.view(torch.int16)), "nothing is left after the close"
+    n_units = L.m_cap + (T + 63) // 64
+    assert int(sig[n_sig + 1]) == n_units
+    m.rdg_fill_i32(sig[n_sig:], 0)
+    m.rdg_combine_finish(y, m.RDG_BF16, L, w, T, K, H, sh, out, m.RDG_BF16, sig, rows)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+    assert not bool(sig[:n_sig].any()), "the tile counters are the down GEMM's; the combine only reads them"
+
+
+def test_finishing_form_argument_checks():
+    m = rdg()
+    T, K, E, H = 8, 2, 4, 256
+    ids = np.tile(np.arange(K, dtype=np.int32), (T, 1))
+    L = m.Layout(m.RDG_CONTIGUOUS, E, T, K, DEV, block_m=16)
+    dummy = torch.zeros((T, 16), dtype=torch.float32, device=DEV)
+    xp = torch.zeros((L.m_cap, 16), dtype=torch.float32, device=DEV)
+    m.rdg_dispatch(dummy, None, m.RDG_F32, torch.from_numpy(ids).to(DEV), L, xp)
+    y = torch.zeros((L.m_cap, H), dtype=torch.bfloat16, device=DEV)
+    w = torch.ones((T, K), dtype=torch.float32, device=DEV)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    sig = torch.zeros((L.m_cap + 2,), dtype=torch.int32, device=DEV)
+    for bad in (dict(signals=None), dict(rows=7), dict(y_dt=m.RDG_F32), dict(K=3)):
+        with pytest.raises(RuntimeError):
+            m.rdg_combine_finish(y, bad.get("y_dt", m.RDG_BF16), L, w, T, bad.get("K", K), H, None, out, m.RDG_BF16,
+                                 bad.get("signals", sig), bad.get("rows", 16))
+    torch.cuda.synchronize()
