@@ -687,8 +687,18 @@ def sbo_compare(b, steps, rounds=4):
             res[mode].append(ms)
     b.sbo_mode = "signalled"
     sig, seq = float(np.median(res["signalled"])), float(np.median(res["sequential"]))
+    # share of the combine's work units the polling workgroups claimed before
+    # the finishing combine closed their counter (its first unit, per step)
+    fracs = []
+    n_sig = (b.L.m_cap + b.signal_rows - 1) // b.signal_rows
+    n_units = b.L.m_cap + (b.T + 63) // 64
+    for _ in range(per):
+        b.step()
+        b.torch.cuda.synchronize()
+        fracs.append(int(b.signals[n_sig + 1].item()) / n_units)
     return {"signalled_ms": sig, "sequential_ms": seq, "gain_ms": seq - sig,
-            "overlap_pays": seq > sig, "rounds": rounds, "steps_per_round": per}
+            "overlap_pays": seq > sig, "rounds": rounds, "steps_per_round": per,
+            "polled_unit_fraction": round(float(np.median(fracs)), 4)}
 
 
 def dispatch_forms(b, reps=20):
