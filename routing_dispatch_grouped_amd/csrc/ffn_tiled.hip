@@ -436,12 +436,6 @@ __global__ __launch_bounds__(NW * 64, 1) void k_ffn_tiled(TArgs a) {
     const Ring ring[3] = {{lx0, ls0, lw0}, {lx1, ls1, lw1}, {lx2, ls0, lw0}};
 
     int fb, tile;
-    // The signalled form claims all 256 registers of its waves (two per SIMD
-    // fill the register file), so that the polling combine running beside
-    // it cannot put a wave on one of its SIMDs: with about 200 registers the
-    // pollers' spinning waves shared its SIMDs and the fp8 rank-share step
-    // took 1.87 ms instead of 1.80.
-    if constexpr (SIGNAL) asm volatile("" ::: "v255");
     if (SIGNAL) {
         // tile-major in dispatch order (grid x = column panel, padded to a
         // multiple of 8): row tiles complete in layout order for the polling
