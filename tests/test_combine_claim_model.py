@@ -4,16 +4,20 @@ request, section 2: the consumer takes each block of rows once its counter
 is complete; here a few polling waves take the blocks that complete early
 and the finishing form the rest).
 
-The polling waves each repeat: claimed = fetch_add(counter, 1); stop if
-claimed < 0 or claimed >= n_units, else combine unit `claimed`.  The
+The polling waves each repeat: claimed = fetch_add(counter, CH); stop if
+claimed < 0 or claimed >= n_units, else combine the units [claimed,
+min(claimed + CH, n_units)).  The kernel claims one unit at a time (CH = 1);
+claims of several units are explored as well, since the partition rule does
+not depend on CH.  The
 finishing form does old = fetch_add(counter, CLOSED) once, sets
 start = old if 0 <= old < n_units else n_units, and combines every unit
 u >= start.  Counters are 32-bit and wrap.  Atomic adds are linearisable, so
 an execution is an interleaving of these adds; every interleaving of a few
 waves, one or more closes and small unit counts is explored, and each must
 combine every unit exactly once.  Seeded mistakes (an off-by-one start, a
-missing exhaustion test, a close that does not stop the waves, a start rule
-without its sign test) are caught, so the model can fail."""
+missing per-unit range test, a close that does not stop the waves, a start
+rule without its sign test, a start rounded to a chunk boundary) are caught,
+so the model can fail."""
 import pytest
 
 CLOSED = 1 << 30
@@ -28,7 +32,8 @@ def kernel_start(old, n_units):
     return old if 0 <= old < n_units else n_units
 
 
-def explore(n_units, n_waves, closes=1, start_rule=kernel_start, stop_rule=None, close_add=CLOSED):
+def explore(n_units, n_waves, closes=1, start_rule=kernel_start, stop_rule=None, close_add=CLOSED, chunk=1,
+            clip=True):
     """Yields, for every schedule, the (unit, who) pairs combined."""
     stop_rule = stop_rule or (lambda c: c < 0 or c >= n_units)
 
@@ -45,8 +50,9 @@ def explore(n_units, n_waves, closes=1, start_rule=kernel_start, stop_rule=None,
                 if stop_rule(claimed):
                     nl[m] = False
                 else:
-                    nd = done + ((claimed, "wave%d" % m),)
-                yield from run(wrap32(counter + 1), tuple(nl), closes_left, nd)
+                    end = min(claimed + chunk, n_units) if clip else claimed + chunk
+                    nd = done + tuple((u, "wave%d" % m) for u in range(claimed, end))
+                yield from run(wrap32(counter + chunk), tuple(nl), closes_left, nd)
             else:
                 s = start_rule(counter, n_units)
                 nd = done + tuple((u, "finish%d" % closes_left) for u in range(n_units) if u >= s)
@@ -69,6 +75,23 @@ def test_every_unit_exactly_once(n_units, n_waves):
     ok, bad, count = all_exactly_once(n_units, n_waves)
     assert ok, bad
     assert count > 1
+
+
+@pytest.mark.parametrize("n_units,n_waves,chunk", [(5, 2, 2), (7, 2, 3), (4, 3, 2), (6, 2, 4), (3, 2, 8)])
+def test_chunked_claims_every_unit_exactly_once(n_units, n_waves, chunk):
+    ok, bad, count = all_exactly_once(n_units, n_waves, chunk=chunk)
+    assert ok, bad
+    ok, bad, _ = all_exactly_once(n_units, n_waves, chunk=chunk, closes=0)
+    assert ok, bad
+    ok, bad, _ = all_exactly_once(n_units, n_waves, chunk=chunk, closes=3)
+    assert ok, bad
+
+
+def test_chunked_claims_with_a_start_inside_a_chunk_are_caught():
+    # a close that took the counter's value rounded down to a chunk boundary
+    # would hand the finishing form units a wave already holds
+    ok, _, _ = all_exactly_once(5, 2, chunk=2, start_rule=lambda old, n: min(old - old % 4, n) if old >= 0 else n)
+    assert not ok
 
 
 @pytest.mark.parametrize("n_units,n_waves", [(2, 2), (3, 2)])
@@ -96,7 +119,11 @@ def test_seeded_mistakes_are_caught(mistake):
     elif mistake == "start_one_early":
         kw["start_rule"] = lambda old, n: max(min(old, n) - 1, 0)
     elif mistake == "no_exhaustion_test":
+        # no per-unit test against n_units (the kernel's lanes each check
+        # theirs): a wave whose claim ends past the units combines phantoms
         kw["stop_rule"] = lambda c: c < 0 or c > n_units
+        kw["clip"] = False
+        kw["chunk"] = 2
     elif mistake == "close_adds_one":
         kw["close_add"] = 1
     elif mistake == "start_without_sign_test":
