@@ -535,11 +535,14 @@ class Bench:
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT)
             return
+        # The shared expert (on the rank's own tokens) runs on the side stream
+        # once the routed gate/up is done, beside the down GEMM: 3% faster
+        # steps than beside the gate/up with fp32 scales, equal with
+        # power-of-two scales.
         if self.sbo_mode == "sequential":
-            # the same step without the overlap: shared expert on the side
-            # stream beside gate/up, then down GEMM and a plain combine
-            self.side.wait_stream(self.stream)
+            # the same step without the overlap: down GEMM and a plain combine
             self._gate_up(timed)
+            self.side.wait_stream(self.stream)
             with self.torch.cuda.stream(self.side):
                 self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y)
@@ -547,11 +550,10 @@ class Bench:
             self.stream.wait_stream(self.side)
             return
         # signalled down GEMM on this stream, then the finishing combine; on
-        # the side stream the shared expert (overlapping gate/up), then the
-        # polling combine, released once gate/up is done so that it overlaps
-        # the down GEMM
+        # the side stream, once gate/up is done, the shared expert and then
+        # the polling combine (it takes the row tiles that complete while it
+        # runs; the finishing combine closes its counter and takes the rest)
         rdg.rdg_fill_i32(self.signals, 0)
-        self.side.wait_stream(self.stream)
         self._gate_up(timed)
         self.gate_done.record(self.stream)
         rdg.rdg_grouped_down(self.L, self.DT, H, I, self.h, self.h_s, self.W["W2"], self.S.get("W2"), self.y,
@@ -559,8 +561,8 @@ class Bench:
         rdg.rdg_combine_finish(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
                                self.signal_rows)
         with self.torch.cuda.stream(self.side):
-            self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             self.side.wait_event(self.gate_done)
+            self._shared(self.x_own, self.x_own_s, cfg["own_tokens"], stream=self.side)
             rdg.rdg_combine(self.y, self.YDT, self.L, self.tw, self.T, K, H, None, self.out, self.YDT, self.signals,
                             self.signal_rows, self.threshold, 1_000_000, self.poll_blocks, stream=self.side)
         self.stream.wait_stream(self.side)
