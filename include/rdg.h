@@ -325,8 +325,9 @@ int rdg_grouped_gate_up_gather(const rdg_layout* L, int dtype, int H, int I, con
 /* Rows per signal counter (the grouped GEMMs' row tile for this layout,
  * type and size: 16, 32, 64 or 128) and the counter value that means "row
  * tile done" (H), for the down GEMM of rdg_grouped_ffn.  With signals, the
- * down GEMM runs its workgroups tile-major, so row tiles complete in layout
- * order; at most 65535 row tiles (RDG_EUNSUPPORTED beyond). */
+ * down GEMM takes the row tiles in layout order (one at a time, or in groups
+ * of a few for the 128-row tiles), so they complete in about that order; at
+ * most 65535 row tiles (RDG_EUNSUPPORTED beyond). */
 int rdg_signal_rows(const rdg_layout* L, int dtype, int H, int I);
 int rdg_signal_threshold(int H, int dtype);
 
