@@ -352,8 +352,28 @@ def test_prefill_rank_fp8_workload_sbo():
 @pytest.mark.parametrize("kind", [0, 1])
 @pytest.mark.parametrize("finish", [False, True])
 def test_sbo_small(dtype, B, kind, finish):
+    _sbo_case(dtype, B, kind, finish)
+
+
+# the 128-row signalled down GEMM takes the row tiles in groups of G in
+# layout order, G = 4 raised until G x (column panels) is a multiple of 8:
+# odd panel counts (G = 8) and tile counts that leave a partial last group
+@pytest.mark.parametrize("dtype,H", [("fp8", 1280), ("fp8", 768), ("bf16", 1536), ("bf16", 1024), ("fp8u", 1280)])
+@pytest.mark.parametrize("B", [1000, 1237])
+def test_sbo_signal_order_groups(dtype, H, B):
+    nt = _sbo_case(dtype, B, 0, True, H=H)
+    panel = 512 if dtype == "bf16" else 256
+    P = H // panel
+    G = 4
+    while (G * P) % 8:
+        G += 1
+    print("row tiles %d, panels %d, group %d" % (nt, P, G), flush=True)
+    assert nt > G
+
+
+def _sbo_case(dtype, B, kind, finish, H=512):
     m = rdg()
-    cfg = _small_cfg(dtype, wid=500 + B + kind)
+    cfg = _small_cfg(dtype, H=H, wid=500 + B + kind + H)
     dt = dt_code(cfg)
     logits = synth.logits(cfg, B)
     ids, w, ri, rw = _route(cfg, logits)
@@ -392,6 +412,7 @@ def test_sbo_small(dtype, B, kind, finish):
     check_rows(got[keep], ref[keep], cfg, "sbo small")
     assert not out_as_f64(got[(loc_np < 0).all(1)]).any(), "tokens without a local row must be zero"
     assert err <= tolerance(cfg), err
+    return int(sum((int(v) + rows - 1) // rows for v in mm))
 
 
 def test_sbo_timeout_is_reported_not_hung():
