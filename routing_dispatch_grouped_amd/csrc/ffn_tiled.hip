@@ -420,8 +420,9 @@ __device__ bool down_split(const TArgs& a, int& fb, int& tile) {
 // takes 0.397 ms this way against 0.436 ms tile-major (panels fb = x mod 8 of
 // every tile on XCD x), 0.399 / 0.409 / 0.418 ms with groups of 2 / 8 / 16
 // tiles, and 0.401 ms in the plain order, where tiles complete only at the
-// end.  Returns false for a block without an item (the grid has
-// n_tiles_max x (P + 1) blocks, at least tiles x P + 8).
+// end.  Returns false for a block without an item.  The grid has
+// n_tiles_max x (P + 1) blocks, at least tiles x (P + 1): every XCD then has
+// at least as many blocks as items.
 __device__ bool signal_order(const TArgs& a, int cols, int& fb, int& tile) {
     const int P = a.Nout / cols, nt = a.tile_off[a.n_local];
     int G = 4;
