@@ -63,6 +63,31 @@ def test_combine_parity(T, K, E, H, ydt, shared):
         assert np.mean(g != ref) < 1e-3
 
 
+@pytest.mark.parametrize("max_blocks", [1, 7, 64, 1000])
+def test_combine_workgroup_cap_is_bit_equal(max_blocks):
+    # a cap on the plain form's workgroups makes each wave walk several
+    # (token, 512-feature slice) units in turn; every unit is still combined
+    # once, in the same slot order
+    m = rdg()
+    T, K, E, H = 700, 8, 32, 2048
+    rng = np.random.default_rng([T, K, E, H, 9])
+    ids = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int32)
+    ids[rng.random(ids.shape) < 0.1] = -1
+    w = torch.from_numpy(rng.random((T, K)).astype(np.float32)).to(DEV)
+    L = m.Layout(m.RDG_CONTIGUOUS, E, T, K, DEV, block_m=16)
+    dummy = torch.zeros((T, 16), dtype=torch.float32, device=DEV)
+    xp = torch.zeros((L.m_cap, 16), dtype=torch.float32, device=DEV)
+    m.rdg_dispatch(dummy, None, m.RDG_F32, torch.from_numpy(ids).to(DEV), L, xp)
+    y = torch.randn((L.m_cap, H), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    sh = torch.randn((T, H), dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    ref = torch.empty((T, H), dtype=torch.bfloat16, device=DEV)
+    got = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device=DEV)
+    m.rdg_combine(y, m.RDG_BF16, L, w, T, K, H, sh, ref, m.RDG_BF16)
+    m.rdg_combine(y, m.RDG_BF16, L, w, T, K, H, sh, got, m.RDG_BF16, max_blocks=max_blocks)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), ref.view(torch.int16))
+
+
 def test_finishing_form_alone_repeated_and_after_polling_stops():
     """rdg_combine_finish with no polling combine beside it takes every token
     (equal to the plain form bit for bit); a second call finds the counter
